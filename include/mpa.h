@@ -1,0 +1,211 @@
+/*
+ * mpa.h -- C ABI of libmpa: masked attention over a paged KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Two operations, each called in two phases like the Ascend ATB C interface
+ * (pages "PrefixEncoder" and "MLA", section 定义 / definition): a first call
+ * validates the arguments, plans the launch on the host and returns an opaque
+ * operation plus the workspace size it needs; a second call runs it
+ * asynchronously on a HIP stream.
+ *
+ *   mpaSelfAttentionPrefixEncoderGetWorkspaceSize / mpaSelfAttentionPrefixEncoder
+ *       fused masked self-attention of new query rows over a paged cache that
+ *       already holds their prefix (ATB page "PrefixEncoder", parameter table);
+ *       causal, right-aligned / sqrt / left-aligned ALiBi and padding masks are
+ *       generated inside the kernel (ATB page "压缩mask", sections 开启方式 and
+ *       约束说明) -- no mask tensor is ever read.
+ *   mpaMLAGetWorkspaceSize / mpaMLA
+ *       split-KV decode of multi-head latent attention: 576-wide query/key
+ *       (qNope 512 + qRope 64), 512-wide latent value, one KV head (ATB page
+ *       "MLA", parameter table).
+ *
+ * Conventions shared by every call:
+ *   - "dev" pointers are HIP device pointers, "HOST" pointers are ordinary host
+ *     memory read during the call that receives them (the host arrays are copied
+ *     into the operation, so the caller may free them afterwards);
+ *   - the caller owns every tensor and the workspace; the library owns only the
+ *     mpaOperation (host object plus a small device copy of its launch plan),
+ *     released by mpaDestroyOperation;
+ *   - all shape and argument checks happen in the first phase, on the host,
+ *     before any HIP call; on error *op is set to NULL and a status != MPA_OK is
+ *     returned; mpaGetLastErrorMessage() then describes the failure (per thread);
+ *   - block ids inside blockTables live on the device and are NOT checked: every
+ *     entry a sequence uses must name a block < numBlocks;
+ *   - the execute phase is asynchronous on the given stream (a hipStream_t, NULL
+ *     = the null stream); every pointer captured in the operation and the
+ *     workspace must stay valid until the stream passes the call.  An operation
+ *     may be executed any number of times; executions on different streams must
+ *     not share a workspace concurrently.
+ */
+#ifndef MPA_H_
+#define MPA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mpaStatus;
+#define MPA_OK 0
+#define MPA_ERROR_INVALID_ARG 1       /* a null required pointer, a bad size or shape */
+#define MPA_ERROR_UNSUPPORTED 2       /* a valid value this build does not implement */
+#define MPA_ERROR_WORKSPACE_TOO_SMALL 3
+#define MPA_ERROR_HIP 4               /* a HIP runtime call failed (message has details) */
+
+typedef struct mpaOperation mpaOperation; /* opaque, library-owned */
+
+/* Element type of query/key/value and of the attention output. */
+#define MPA_FP16 0
+#define MPA_BF16 1
+
+/* PrefixEncoder maskType.  3, 4, 5 and 9 carry the numbers of the ATB
+ * PrefixEncoder parameter table (row maskType); 0 is this library's: no causal
+ * rule, keys limited only by kvSeqLen (padding mask).  The ATB compressed norm
+ * mask used for RoPE models (MASK_TYPE_NORM_COMPRESS, number not given on the
+ * pages) has causal semantics: pass MPA_MASK_CAUSAL. */
+#define MPA_MASK_NONE 0
+#define MPA_MASK_ALIBI_COMPRESS 3            /* bias slope_h * (j - a_i), causal */
+#define MPA_MASK_ALIBI_COMPRESS_SQRT 4       /* bias -slope_h * sqrt(a_i - j), causal */
+#define MPA_MASK_ALIBI_COMPRESS_LEFT_ALIGN 5 /* bias slope_h * j, causal */
+#define MPA_MASK_CAUSAL 9                    /* generated inside the operator */
+
+/*
+ * PrefixEncoder, phase 1.  Sequence b has seqLen[b] new query rows and
+ * kvSeqLen[b] >= seqLen[b] keys in the paged cache; the first kvSeqLen[b] -
+ * seqLen[b] keys are its cached prefix and its query row i sits at absolute
+ * position a_i = kvSeqLen[b] - seqLen[b] + i (ATB page "PrefixEncoder",
+ * parameter table, rows seqLen and kvSeqLen).  For every query head h and
+ * row i it computes
+ *     s_j  = qkScale * (q_i . k_j) + bias(i, j)     over the visible keys j
+ *     out_i = sum_j softmax(s)_j v_j,   lse_i = ln sum_j exp(s_j)
+ * with key j of sequence b at key[blockTables[b][j / blockSize]][j % blockSize]
+ * [h / (headNum / kvHeadNum)] (GQA, contiguous head groups).  Visible: j <
+ * kvSeqLen[b] and, for maskType 3/4/5/9, j <= a_i.
+ *
+ *   query        dev  [nTokens, headNum, headSize]  dtype; sequence b's rows
+ *                     start at row qStartLoc[b] (or packed, see qStartLoc)
+ *   key, value   dev  [numBlocks, blockSize, kvHeadNum, headSize] dtype
+ *   blockTables  dev  [batch, maxBlockNum] int32; entries at and beyond
+ *                     ceil(kvSeqLen[b] / blockSize) are never read
+ *   seqLen       HOST [batch] int32, >= 0
+ *   kvSeqLen     HOST [batch] int32, >= seqLen[b], ceil(kvSeqLen/blockSize) <= maxBlockNum
+ *   slopes       dev  [headNum] fp32 ALiBi coefficients; required for maskType
+ *                     3/4/5, must be NULL otherwise
+ *   maskType     one of MPA_MASK_*
+ *   headNum      query heads (> 0); kvHeadNum KV heads, headNum % kvHeadNum == 0
+ *   qkScale      scale applied to q.k before the bias
+ *   batch        number of sequences (>= 1)
+ *   headSize     64 or 128
+ *   numBlocks, blockSize, maxBlockNum   paged cache geometry (blockSize >= 1)
+ *   dtype        MPA_FP16 or MPA_BF16
+ *   qStartLoc    HOST [batch] int64 first query row of each sequence, or NULL
+ *                for the packed layout (prefix sums of seqLen).  With a padded
+ *                layout (qStartLoc[b] = b * Lpad) the rows between sequences
+ *                are neither read nor written.
+ *   nTokens      rows of query and attnOut (>= every qStartLoc[b] + seqLen[b])
+ *   attnOut      dev  [nTokens, headNum, headSize] dtype (output)
+ *   lse          dev  [nTokens, headNum] fp32 natural-log LSE (output), or NULL
+ *   workspaceSize, op  outputs: bytes of device workspace phase 2 needs (0 for
+ *                this operation) and the new operation
+ */
+mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
+    const void *query, const void *key, const void *value, const int32_t *blockTables,
+    const int32_t *seqLen, const int32_t *kvSeqLen, const float *slopes, int maskType,
+    int32_t headNum, int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
+    int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum, int dtype,
+    const int64_t *qStartLoc, int64_t nTokens, void *attnOut, float *lse,
+    uint64_t *workspaceSize, mpaOperation **op);
+
+/* PrefixEncoder, phase 2: launch on `stream` (hipStream_t).  `workspace` may be
+ * NULL when the size phase 1 returned is 0. */
+mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
+                                        mpaOperation *op, void *stream);
+
+/* MLA maskType / calcType / cacheMode (ATB page "MLA", parameter table).  Only
+ * CALC_TYPE_UNDEFINED = 0 and KVCACHE = 0 carry numbers on the page; the others
+ * follow the order the page lists them in. */
+#define MPA_MLA_MASK_UNDEFINED 0   /* all-zero mask: every token sees keys < contextLens */
+#define MPA_MLA_MASK_SPEC 1        /* token t of q_len sees keys j <= contextLens - q_len + t */
+#define MPA_MLA_CALC_UNDEFINED 0   /* one query token per sequence */
+#define MPA_MLA_CALC_SPEC 1        /* qSeqLen tokens per sequence (speculative decode) */
+#define MPA_MLA_CACHE_KVCACHE 0    /* one concatenated cache ctKV [NB, BS, 1, 576], kRope NULL */
+#define MPA_MLA_CACHE_KROPE_CTKV 1 /* separate ctKV [NB, BS, 1, 512] and kRope [NB, BS, 1, 64] */
+
+/*
+ * MLA, phase 1.  Query token t of sequence b (tokens are batch-major: the
+ * qSeqLen[b] tokens of sequence b follow those of b - 1) and head h attend
+ * over keys j < contextLens[b] of the one latent KV head:
+ *     s_j = qkScale * ([qNope|qRope]_{t,h} . [ctKV|kRope]_j),
+ *     attenOut_{t,h} = sum_j softmax(s)_j ctKV_j[0:512],  lse = ln sum_j exp(s_j)
+ * with the visibility of maskType.  The keys of a sequence are split over
+ * several workgroups; their partial results are merged by their LSE.
+ *
+ *   qNope      dev [T, headNum, 512] dtype     qRope  dev [T, headNum, 64] dtype
+ *   ctKV       dev [numBlocks, blockSize, 1, 512] (cacheMode 1) or
+ *                  [numBlocks, blockSize, 1, 576] (cacheMode 0) dtype
+ *   kRope      dev [numBlocks, blockSize, 1, 64] dtype (cacheMode 1), NULL for 0
+ *   blockTables dev [batch, maxBlockNum] int32
+ *   contextLens HOST [batch] int32 >= 1 (keys of each sequence, speculative
+ *               tokens included)
+ *   qSeqLen    HOST [batch] int32 in [1, contextLens[b]]; required iff calcType
+ *              is MPA_MLA_CALC_SPEC, else NULL (one token per sequence)
+ *   headNum    query heads (1..128 per token; > 0); kvHeadNum must be 1
+ *   qkScale, maskType, calcType, cacheMode  see above (the int8 / NZ cache modes
+ *              2 and 3 and calcType RING / PREFILL return MPA_ERROR_UNSUPPORTED)
+ *   batch, numBlocks, blockSize, maxBlockNum, dtype   as for PrefixEncoder
+ *   attenOut   dev [T, headNum, 512] dtype (output)
+ *   lse        dev [T, headNum] fp32 natural-log LSE (output), or NULL
+ *   workspaceSize, op  outputs: device workspace bytes (split-KV partial
+ *              results) and the new operation
+ */
+mpaStatus mpaMLAGetWorkspaceSize(
+    const void *qNope, const void *qRope, const void *ctKV, const void *kRope,
+    const int32_t *blockTables, const int32_t *contextLens, const int32_t *qSeqLen,
+    int32_t headNum, float qkScale, int32_t kvHeadNum, int maskType, int calcType,
+    int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum,
+    int dtype, void *attenOut, float *lse, uint64_t *workspaceSize, mpaOperation **op);
+
+/* MLA, phase 2: two launches on `stream` -- split-KV partials into the
+ * workspace (>= the size phase 1 returned, 256-byte aligned), then their
+ * LSE-weighted merge into attenOut / lse. */
+mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void *stream);
+
+/* Releases an operation (NULL is accepted).  Must not be called while an
+ * execution of it may still be running on a stream. */
+mpaStatus mpaDestroyOperation(mpaOperation *op);
+
+/* Static description of a status code. */
+const char *mpaGetErrorString(mpaStatus status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *mpaGetLastErrorMessage(void);
+
+/*
+ * Host-only inspection of the PrefixEncoder launch plan (no HIP call; for tests
+ * and tools).  Fills items[0 .. *nItems) with 4 int32 each, one per workgroup in
+ * launch order: {b, first query head, first query row, number of key tiles the
+ * workgroup visits}, and reports the tile geometry.  Returns
+ * MPA_ERROR_INVALID_ARG if capacity (in items) is too small; *nItems is set
+ * either way.
+ */
+mpaStatus mpaPrefixEncoderPlanInspect(const int32_t *seqLen, const int32_t *kvSeqLen,
+                                      int32_t batch, int maskType, int32_t headNum,
+                                      int32_t kvHeadNum, int32_t headSize, int32_t *items,
+                                      int64_t capacity, int64_t *nItems, int32_t *rowsPerItem,
+                                      int32_t *keysPerTile, int32_t *headsPerItem);
+
+/*
+ * Host-only inspection of the MLA split plan.  Fills splits[0 .. *nSplits) with
+ * 4 int32 each: {b, first key, end key, index of this split among the splits of
+ * sequence b}, in launch order.
+ */
+mpaStatus mpaMLAPlanInspect(const int32_t *contextLens, const int32_t *qSeqLen, int32_t batch,
+                            int32_t headNum, int calcType, int32_t *splits, int64_t capacity,
+                            int64_t *nSplits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPA_H_ */

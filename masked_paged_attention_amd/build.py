@@ -1,0 +1,72 @@
+"""Builds libmpa.so (the C ABI of include/mpa.h) for gfx950 with hipcc, in-tree.
+
+    python -m masked_paged_attention_amd.build      # or build_library() from Python
+
+Sources are compiled in parallel into masked_paged_attention_amd/_build/ and
+linked into masked_paged_attention_amd/lib/libmpa.so.  Every call recompiles.
+"""
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libmpa.so")
+
+SOURCES = ["api.cpp", "planner.cpp", "prefill_fwd.hip", "mla_decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else (shutil.which("hipcc") or "hipcc")
+
+
+def common_flags():
+    # Packed fp32 VALU ops are disabled for all device code.
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+            "-Wno-unused-command-line-argument"]
+
+
+def _compile(src):
+    out = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", out]
+    if src.endswith(".cpp"):
+        cmd.insert(1, "-x")
+        cmd.insert(2, "hip")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+    return out
+
+
+def build_library(verbose=True):
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library()
+    sys.exit(0)

@@ -1,0 +1,439 @@
+// C ABI of libmpa (declared in include/mpa.h): argument validation, operation
+// objects holding the launch plan, and the launches.
+//
+// Phase 1 (…GetWorkspaceSize) validates every argument on the host first --
+// nothing touches HIP until all checks pass -- then plans the launch on the host
+// and uploads the plan once into a small device buffer owned by the operation.
+// Phase 2 is then a pure launch (no copy, no allocation): one kernel for the
+// prefix encoder, split + combine for MLA.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mpa.h"
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mpaStatus fail(mpaStatus st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mpaStatus hip_fail(hipError_t e, const char* what) {
+  return fail(MPA_ERROR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+int shift_of(int bs) {
+  if (bs > 0 && (bs & (bs - 1)) == 0) {
+    int s = 0;
+    while ((1 << s) < bs) ++s;
+    return s;
+  }
+  return -1;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+struct mpaOperation {
+  enum Kind { kPrefill, kMla } kind;
+  int dtype = 0;
+  // prefill
+  mpa::PrefillParams pp{};
+  int head_size = 0;
+  int mask_type = 0;
+  int grid = 0;
+  // mla
+  mpa::MlaParams mp{};
+  uint64_t ws_bytes = 0;
+  uint64_t part_o_off = 0, part_lse_off = 0;
+  // device copy of the plan
+  void* dplan = nullptr;
+  int device = 0;
+
+  ~mpaOperation() {
+    if (dplan) {
+      int cur = 0;
+      if (hipGetDevice(&cur) == hipSuccess && cur != device) {
+        (void)hipSetDevice(device);
+        (void)hipFree(dplan);
+        (void)hipSetDevice(cur);
+      } else {
+        (void)hipFree(dplan);
+      }
+    }
+  }
+};
+
+namespace {
+
+// Copies a host plan (a list of byte blobs, each 16-byte aligned) to the device
+// in one allocation; returns the device base and the blob offsets.
+mpaStatus upload(mpaOperation* op, const std::vector<std::pair<const void*, size_t>>& blobs,
+                 std::vector<size_t>& offs) {
+  size_t total = 0;
+  offs.clear();
+  for (auto& bl : blobs) {
+    offs.push_back(total);
+    total += (bl.second + 255) & ~size_t(255);
+  }
+  std::vector<char> host(total ? total : 16, 0);
+  for (size_t i = 0; i < blobs.size(); ++i)
+    if (blobs[i].second) std::memcpy(host.data() + offs[i], blobs[i].first, blobs[i].second);
+  hipError_t e = hipGetDevice(&op->device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipMalloc(&op->dplan, host.size());
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc (operation plan)");
+  e = hipMemcpy(op->dplan, host.data(), host.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (operation plan)");
+  return MPA_OK;
+}
+
+mpaStatus check_prefill(const void* query, const void* key, const void* value,
+                        const int32_t* blockTables, const int32_t* seqLen, const int32_t* kvSeqLen,
+                        const float* slopes, int maskType, int32_t headNum, int32_t kvHeadNum,
+                        float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks,
+                        int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
+                        int64_t nTokens, void* attnOut, uint64_t* workspaceSize, mpaOperation** op) {
+  if (!op || !workspaceSize) return fail(MPA_ERROR_INVALID_ARG, "workspaceSize and op must not be NULL");
+  if (!query || !key || !value || !blockTables || !attnOut)
+    return fail(MPA_ERROR_INVALID_ARG, "query, key, value, blockTables and attnOut are required");
+  if (!seqLen || !kvSeqLen) return fail(MPA_ERROR_INVALID_ARG, "seqLen and kvSeqLen (host) are required");
+  if (batch < 1) return fail(MPA_ERROR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  if (headNum <= 0) return fail(MPA_ERROR_INVALID_ARG, "headNum must be > 0 (got %d)", headNum);
+  if (kvHeadNum <= 0 || headNum % kvHeadNum != 0)
+    return fail(MPA_ERROR_INVALID_ARG, "kvHeadNum must be > 0 and divide headNum (%d / %d)", headNum,
+                kvHeadNum);
+  if (dtype != MPA_FP16 && dtype != MPA_BF16)
+    return fail(MPA_ERROR_INVALID_ARG, "dtype must be MPA_FP16 or MPA_BF16 (got %d)", dtype);
+  if (maskType != MPA_MASK_NONE && maskType != MPA_MASK_ALIBI_COMPRESS &&
+      maskType != MPA_MASK_ALIBI_COMPRESS_SQRT && maskType != MPA_MASK_ALIBI_COMPRESS_LEFT_ALIGN &&
+      maskType != MPA_MASK_CAUSAL)
+    return fail(MPA_ERROR_UNSUPPORTED, "maskType %d is not supported (0, 3, 4, 5, 9)", maskType);
+  const bool alibi = maskType == MPA_MASK_ALIBI_COMPRESS || maskType == MPA_MASK_ALIBI_COMPRESS_SQRT ||
+                     maskType == MPA_MASK_ALIBI_COMPRESS_LEFT_ALIGN;
+  if (alibi && !slopes) return fail(MPA_ERROR_INVALID_ARG, "ALiBi mask types need slopes");
+  if (!alibi && slopes) return fail(MPA_ERROR_INVALID_ARG, "slopes must be NULL for maskType %d", maskType);
+  if (headSize != 64 && headSize != 128)
+    return fail(MPA_ERROR_UNSUPPORTED, "headSize %d is not supported (64 or 128)", headSize);
+  if (!(qkScale == qkScale) || qkScale == INFINITY || qkScale == -INFINITY)
+    return fail(MPA_ERROR_INVALID_ARG, "qkScale must be finite");
+  if (numBlocks < 1 || blockSize < 1 || maxBlockNum < 1)
+    return fail(MPA_ERROR_INVALID_ARG, "numBlocks, blockSize and maxBlockNum must be >= 1");
+  if (nTokens < 0) return fail(MPA_ERROR_INVALID_ARG, "nTokens must be >= 0");
+  int64_t packed = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = seqLen[b], kv = kvSeqLen[b];
+    if (L < 0 || kv < L)
+      return fail(MPA_ERROR_INVALID_ARG, "sequence %d: need 0 <= seqLen (%lld) <= kvSeqLen (%lld)", b,
+                  (long long)L, (long long)kv);
+    if ((kv + blockSize - 1) / blockSize > maxBlockNum)
+      return fail(MPA_ERROR_INVALID_ARG, "sequence %d: kvSeqLen %lld needs more than maxBlockNum=%d blocks",
+                  b, (long long)kv, maxBlockNum);
+    const int64_t start = qStartLoc ? qStartLoc[b] : packed;
+    if (start < 0 || start + L > nTokens)
+      return fail(MPA_ERROR_INVALID_ARG, "sequence %d: rows [%lld, %lld) exceed nTokens=%lld", b,
+                  (long long)start, (long long)(start + L), (long long)nTokens);
+    packed += L;
+  }
+  if (qStartLoc) {
+    // Row ranges of different sequences must not overlap (outputs would race).
+    std::vector<std::pair<int64_t, int64_t>> r;
+    for (int b = 0; b < batch; ++b)
+      if (seqLen[b] > 0) r.push_back({qStartLoc[b], qStartLoc[b] + seqLen[b]});
+    std::sort(r.begin(), r.end());
+    for (size_t i = 1; i < r.size(); ++i)
+      if (r[i].first < r[i - 1].second)
+        return fail(MPA_ERROR_INVALID_ARG, "qStartLoc: row ranges of two sequences overlap");
+  }
+  return MPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mpaGetErrorString(mpaStatus s) {
+  switch (s) {
+    case MPA_OK: return "success";
+    case MPA_ERROR_INVALID_ARG: return "invalid argument";
+    case MPA_ERROR_UNSUPPORTED: return "unsupported argument value";
+    case MPA_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MPA_ERROR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mpaGetLastErrorMessage(void) { return g_last_error.c_str(); }
+
+mpaStatus mpaDestroyOperation(mpaOperation* op) {
+  delete op;
+  return MPA_OK;
+}
+
+mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
+    const void* query, const void* key, const void* value, const int32_t* blockTables,
+    const int32_t* seqLen, const int32_t* kvSeqLen, const float* slopes, int maskType,
+    int32_t headNum, int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
+    int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
+    int64_t nTokens, void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  mpaStatus st = check_prefill(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType,
+                               headNum, kvHeadNum, qkScale, batch, headSize, numBlocks, blockSize,
+                               maxBlockNum, dtype, qStartLoc, nTokens, attnOut, workspaceSize, op);
+  if (st != MPA_OK) return st;
+
+  const bool causal = maskType != MPA_MASK_NONE;
+  mpa::PrefillPlan plan = mpa::plan_prefill(seqLen, kvSeqLen, batch, causal, headNum, kvHeadNum);
+  std::vector<int32_t> seqs(4 * (size_t)batch);
+  int64_t packed = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t start = qStartLoc ? qStartLoc[b] : packed;
+    packed += seqLen[b];
+    seqs[4 * b + 0] = seqLen[b];
+    seqs[4 * b + 1] = kvSeqLen[b];
+    seqs[4 * b + 2] = (int32_t)(uint32_t)(start & 0xffffffffll);
+    seqs[4 * b + 3] = (int32_t)(start >> 32);
+  }
+  mpaOperation* o = new (std::nothrow) mpaOperation();
+  if (!o) return fail(MPA_ERROR_HIP, "out of host memory");
+  o->kind = mpaOperation::kPrefill;
+  o->dtype = dtype;
+  o->head_size = headSize;
+  o->mask_type = maskType;
+  o->grid = (int)plan.items.size();
+  std::vector<size_t> offs;
+  st = upload(o, {{plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem)},
+                  {seqs.data(), seqs.size() * sizeof(int32_t)}},
+              offs);
+  if (st != MPA_OK) {
+    delete o;
+    return st;
+  }
+  mpa::PrefillParams& p = o->pp;
+  p.q = query;
+  p.k = key;
+  p.v = value;
+  p.out = attnOut;
+  p.lse = lse;
+  p.block_tables = blockTables;
+  p.slopes = slopes;
+  p.items = (const int4*)((char*)o->dplan + offs[0]);
+  p.seqs = (const int4*)((char*)o->dplan + offs[1]);
+  p.head_num = headNum;
+  p.kv_head_num = kvHeadNum;
+  p.block_size = blockSize;
+  p.bs_shift = shift_of(blockSize);
+  p.max_blocks = maxBlockNum;
+  p.heads_per_item = plan.heads_per_item;
+  p.scale2 = qkScale * kLog2e;
+  *workspaceSize = 0;
+  *op = o;
+  return MPA_OK;
+}
+
+mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize, mpaOperation* op,
+                                        void* stream) {
+  (void)workspace;
+  (void)workspaceSize;
+  g_last_error.clear();
+  if (!op || op->kind != mpaOperation::kPrefill)
+    return fail(MPA_ERROR_INVALID_ARG, "op is not a PrefixEncoder operation");
+  hipError_t e = mpa::launch_prefill(op->pp, op->dtype, op->head_size, op->mask_type, op->grid,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return MPA_OK;
+}
+
+mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const void* ctKV,
+                                 const void* kRope, const int32_t* blockTables,
+                                 const int32_t* contextLens, const int32_t* qSeqLen, int32_t headNum,
+                                 float qkScale, int32_t kvHeadNum, int maskType, int calcType,
+                                 int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
+                                 int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
+                                 uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  if (!op || !workspaceSize) return fail(MPA_ERROR_INVALID_ARG, "workspaceSize and op must not be NULL");
+  if (!qNope || !qRope || !ctKV || !blockTables || !attenOut)
+    return fail(MPA_ERROR_INVALID_ARG, "qNope, qRope, ctKV, blockTables and attenOut are required");
+  if (!contextLens) return fail(MPA_ERROR_INVALID_ARG, "contextLens (host) is required");
+  if (batch < 1) return fail(MPA_ERROR_INVALID_ARG, "batch must be >= 1");
+  if (headNum <= 0) return fail(MPA_ERROR_INVALID_ARG, "headNum must be > 0");
+  if (kvHeadNum != 1) return fail(MPA_ERROR_UNSUPPORTED, "MLA supports kvHeadNum == 1 only (got %d)", kvHeadNum);
+  if (dtype != MPA_FP16 && dtype != MPA_BF16) return fail(MPA_ERROR_INVALID_ARG, "dtype must be fp16 or bf16");
+  if (cacheMode != MPA_MLA_CACHE_KVCACHE && cacheMode != MPA_MLA_CACHE_KROPE_CTKV)
+    return fail(MPA_ERROR_UNSUPPORTED, "cacheMode %d is not supported (0, 1)", cacheMode);
+  if (cacheMode == MPA_MLA_CACHE_KROPE_CTKV && !kRope)
+    return fail(MPA_ERROR_INVALID_ARG, "cacheMode 1 needs kRope");
+  if (cacheMode == MPA_MLA_CACHE_KVCACHE && kRope)
+    return fail(MPA_ERROR_INVALID_ARG, "cacheMode 0 keeps the rope part inside ctKV: kRope must be NULL");
+  if (calcType != MPA_MLA_CALC_UNDEFINED && calcType != MPA_MLA_CALC_SPEC)
+    return fail(MPA_ERROR_UNSUPPORTED, "calcType %d is not supported (0, 1)", calcType);
+  if (maskType != MPA_MLA_MASK_UNDEFINED && maskType != MPA_MLA_MASK_SPEC)
+    return fail(MPA_ERROR_UNSUPPORTED, "maskType %d is not supported (0, 1)", maskType);
+  if (calcType == MPA_MLA_CALC_SPEC && !qSeqLen)
+    return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
+  if (calcType == MPA_MLA_CALC_UNDEFINED && qSeqLen)
+    return fail(MPA_ERROR_INVALID_ARG, "qSeqLen must be NULL unless calcType is SPEC");
+  if (!(qkScale == qkScale) || qkScale == INFINITY || qkScale == -INFINITY)
+    return fail(MPA_ERROR_INVALID_ARG, "qkScale must be finite");
+  if (numBlocks < 1 || blockSize < 1 || maxBlockNum < 1)
+    return fail(MPA_ERROR_INVALID_ARG, "numBlocks, blockSize and maxBlockNum must be >= 1");
+  std::vector<int32_t> qlen(batch, 1);
+  for (int b = 0; b < batch; ++b) {
+    if (qSeqLen) qlen[b] = qSeqLen[b];
+    if (contextLens[b] < 1) return fail(MPA_ERROR_INVALID_ARG, "sequence %d: contextLens must be >= 1", b);
+    if (qlen[b] < 1 || qlen[b] > contextLens[b])
+      return fail(MPA_ERROR_INVALID_ARG, "sequence %d: need 1 <= qSeqLen (%d) <= contextLens (%d)", b,
+                  qlen[b], contextLens[b]);
+    if ((int64_t)(contextLens[b] + blockSize - 1) / blockSize > maxBlockNum)
+      return fail(MPA_ERROR_INVALID_ARG, "sequence %d: contextLens %d needs more than maxBlockNum=%d blocks",
+                  b, contextLens[b], maxBlockNum);
+  }
+
+  int dev = 0, cus = 256;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 2 * cus, 32, 64);
+  std::vector<int32_t> seqs(4 * (size_t)batch), seqs2(4 * (size_t)batch, 0);
+  for (int b = 0; b < batch; ++b) {
+    seqs[4 * b + 0] = plan.seqs[b].ctx;
+    seqs[4 * b + 1] = plan.seqs[b].q_len;
+    seqs[4 * b + 2] = plan.seqs[b].tok0;
+    seqs[4 * b + 3] = plan.seqs[b].n_splits;
+    seqs2[4 * b + 0] = plan.seqs[b].split0;
+  }
+  mpaOperation* o = new (std::nothrow) mpaOperation();
+  if (!o) return fail(MPA_ERROR_HIP, "out of host memory");
+  o->kind = mpaOperation::kMla;
+  o->dtype = dtype;
+  std::vector<size_t> offs;
+  mpaStatus st = upload(o, {{plan.splits.data(), plan.splits.size() * sizeof(mpa::MlaSplit)},
+                            {seqs.data(), seqs.size() * 4},
+                            {seqs2.data(), seqs2.size() * 4},
+                            {plan.seq_splits.data(), plan.seq_splits.size() * 4}},
+                        offs);
+  if (st != MPA_OK) {
+    delete o;
+    return st;
+  }
+  mpa::MlaParams& p = o->mp;
+  p.q_nope = qNope;
+  p.q_rope = qRope;
+  p.ckv = ctKV;
+  p.krope = kRope;
+  p.block_tables = blockTables;
+  p.splits = (const int4*)((char*)o->dplan + offs[0]);
+  p.seqs = (const int4*)((char*)o->dplan + offs[1]);
+  p.seqs2 = (const int4*)((char*)o->dplan + offs[2]);
+  p.seq_splits = (const int32_t*)((char*)o->dplan + offs[3]);
+  p.out = attenOut;
+  p.lse = lse;
+  p.head_num = headNum;
+  p.block_size = blockSize;
+  p.bs_shift = shift_of(blockSize);
+  p.max_blocks = maxBlockNum;
+  p.ckv_stride = cacheMode == MPA_MLA_CACHE_KVCACHE ? 576 : 512;
+  p.spec_mask = maskType == MPA_MLA_MASK_SPEC ? 1 : 0;
+  p.n_splits = (int)plan.splits.size();
+  p.row_groups = plan.row_groups;
+  p.tokens = (int)plan.tokens;
+  p.batch = batch;
+  p.scale2 = qkScale * kLog2e;
+  o->part_o_off = 0;
+  o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 4 + 255) & ~uint64_t(255);
+  o->ws_bytes = o->part_lse_off + (((uint64_t)plan.part_rows * 4 + 255) & ~uint64_t(255));
+  *workspaceSize = o->ws_bytes;
+  *op = o;
+  return MPA_OK;
+}
+
+mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void* stream) {
+  g_last_error.clear();
+  if (!op || op->kind != mpaOperation::kMla) return fail(MPA_ERROR_INVALID_ARG, "op is not an MLA operation");
+  if (workspaceSize < op->ws_bytes)
+    return fail(MPA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes, %llu needed",
+                (unsigned long long)workspaceSize, (unsigned long long)op->ws_bytes);
+  if (op->ws_bytes && !workspace) return fail(MPA_ERROR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace) & 255) return fail(MPA_ERROR_INVALID_ARG, "workspace must be 256-byte aligned");
+  mpa::MlaParams p = op->mp;
+  p.part_o = (float*)((char*)workspace + op->part_o_off);
+  p.part_lse = (float*)((char*)workspace + op->part_lse_off);
+  hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "MLA launch");
+  return MPA_OK;
+}
+
+mpaStatus mpaPrefixEncoderPlanInspect(const int32_t* seqLen, const int32_t* kvSeqLen, int32_t batch,
+                                      int maskType, int32_t headNum, int32_t kvHeadNum,
+                                      int32_t headSize, int32_t* items, int64_t capacity,
+                                      int64_t* nItems, int32_t* rowsPerItem, int32_t* keysPerTile,
+                                      int32_t* headsPerItem) {
+  g_last_error.clear();
+  (void)headSize;
+  if (!seqLen || !kvSeqLen || batch < 1 || headNum <= 0 || kvHeadNum <= 0 || headNum % kvHeadNum)
+    return fail(MPA_ERROR_INVALID_ARG, "invalid lengths or head counts");
+  mpa::PrefillPlan plan =
+      mpa::plan_prefill(seqLen, kvSeqLen, batch, maskType != MPA_MASK_NONE, headNum, kvHeadNum);
+  if (nItems) *nItems = (int64_t)plan.items.size();
+  if (rowsPerItem) *rowsPerItem = plan.rows_per_item;
+  if (keysPerTile) *keysPerTile = mpa::kKeysPerTile;
+  if (headsPerItem) *headsPerItem = plan.heads_per_item;
+  if (!items || capacity < (int64_t)plan.items.size())
+    return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu items", (long long)capacity, plan.items.size());
+  std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem));
+  return MPA_OK;
+}
+
+mpaStatus mpaMLAPlanInspect(const int32_t* contextLens, const int32_t* qSeqLen, int32_t batch,
+                            int32_t headNum, int calcType, int32_t* splits, int64_t capacity,
+                            int64_t* nSplits) {
+  g_last_error.clear();
+  if (!contextLens || batch < 1 || headNum <= 0) return fail(MPA_ERROR_INVALID_ARG, "invalid arguments");
+  std::vector<int32_t> qlen(batch, 1);
+  if (calcType == MPA_MLA_CALC_SPEC) {
+    if (!qSeqLen) return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
+    for (int b = 0; b < batch; ++b) qlen[b] = qSeqLen[b];
+  }
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 512, 32, 64);
+  if (nSplits) *nSplits = (int64_t)plan.splits.size();
+  if (!splits || capacity < (int64_t)plan.splits.size())
+    return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu splits", (long long)capacity, plan.splits.size());
+  for (size_t i = 0; i < plan.splits.size(); ++i) {
+    const mpa::MlaSplit& s = plan.splits[i];
+    int idx = -1;
+    if (s.b >= 0) {
+      const mpa::MlaSeq& q = plan.seqs[s.b];
+      for (int k = 0; k < q.n_splits; ++k)
+        if (plan.seq_splits[q.split0 + k] == (int32_t)i) idx = k;
+    }
+    splits[4 * i + 0] = s.b;
+    splits[4 * i + 1] = s.k0;
+    splits[4 * i + 2] = s.k1;
+    splits[4 * i + 3] = idx;
+  }
+  return MPA_OK;
+}
+
+}  // extern "C"

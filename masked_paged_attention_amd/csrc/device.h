@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the MFMA
+// wrappers, the LDS transpose read, cross-half wave reductions and conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<_Float16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+};
+template <>
+struct Vec<__bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+};
+
+// D(32x32, fp32) += A(32x16) * B(16x32).  Lane l supplies A row l%32 and B column
+// l%32, each with the 8 contraction indices of half l/32; lane l receives
+// D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r (layout checked on gfx950).
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of 16-bit data.  In each group of 16 lanes, source lane s
+// points at 4 consecutive elements (row s/4, columns 4*(s%4)..+3 of a 4 x 16
+// block); lane i of the group receives column i of the block's 4 rows.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
+}
+
+// x combined with the value lane l^32 holds (one permlane32 swap).
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+template <typename T>
+__device__ __forceinline__ T to_elem(float x) {
+  return (T)x;  // round to nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32)
+}
+
+// Rounds 8 fp32 values to one MFMA operand (round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x8 pack8(const float* x) {
+  typename Vec<T>::x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (T)x[e];
+  return v;
+}
+
+}  // namespace mpa

@@ -1,0 +1,62 @@
+// Kernel parameter blocks and host launchers shared by api.cpp and the .hip
+// kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpa {
+
+struct PrefillParams {
+  const void* q;               // [nTokens, headNum, D]
+  const void* k;               // [numBlocks, blockSize, kvHeadNum, D]
+  const void* v;
+  void* out;                   // [nTokens, headNum, D]
+  float* lse;                  // [nTokens, headNum] or null
+  const int32_t* block_tables; // [batch, maxBlocks]
+  const float* slopes;         // [headNum] or null
+  const int4* items;           // launch plan: {b, head0, row0, n_tiles}
+  const int4* seqs;            // per sequence: {seqLen, kvSeqLen, qStart lo, qStart hi}
+  int head_num;
+  int kv_head_num;
+  int block_size;
+  int bs_shift;                // log2(blockSize) when a power of two, else -1
+  int max_blocks;
+  int heads_per_item;
+  float scale2;                // qkScale * log2(e)
+};
+
+// dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9.
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
+                          int grid, hipStream_t stream);
+
+struct MlaParams {
+  const void* q_nope;          // [T, H, 512]
+  const void* q_rope;          // [T, H, 64]
+  const void* ckv;             // [NB, BS, 1, ckv_stride] (512 or 576 wide)
+  const void* krope;           // [NB, BS, 1, 64], or null when the rope part sits in ckv
+  const int32_t* block_tables; // [batch, maxBlocks]
+  const int4* splits;          // {b, k0, k1, part_row}
+  const int4* seqs;            // per sequence: {ctx, q_len, tok0, n_splits} (first int4)
+  const int4* seqs2;           // per sequence: {split0 in seq_splits, part_row0, 0, 0}
+  const int32_t* seq_splits;   // split indices of each sequence
+  float* part_o;               // [part_rows, 512] fp32 workspace
+  float* part_lse;             // [part_rows] fp32 workspace
+  void* out;                   // [T, H, 512]
+  float* lse;                  // [T, H] or null
+  int head_num;
+  int block_size;
+  int bs_shift;
+  int max_blocks;
+  int ckv_stride;              // elements per cache row of ckv (512 or 576)
+  int spec_mask;               // 1: token t sees keys <= ctx - q_len + t
+  int n_splits;                // grid x of the split kernel
+  int row_groups;              // grid y of the split kernel
+  int tokens;
+  int batch;
+  float scale2;                // qkScale * log2(e)
+};
+
+hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream);
+
+}  // namespace mpa

@@ -1,0 +1,310 @@
+// Fused masked attention over a paged KV cache (prefill / prefix encoder) for
+// gfx950.
+//
+// What it computes (Ascend ATB page "PrefixEncoder", parameter table; masks of
+// the ATB page "压缩mask", sections 开启方式 and 约束说明; the formula
+// softmax(QK^T * scale + M) V of the nalar.dev padding-mask article, section
+// "Masking mengubah kelayakan relasi attention"): for each sequence b, query
+// head h and new row i (absolute position a = kvSeqLen - seqLen + i)
+//   s_j = qkScale * q.k_j + bias(a, j) over visible keys j,  o = softmax(s) V,
+//   lse = ln sum_j exp(s_j).
+// Visibility and bias are generated in registers from (maskType, slopes,
+// seqLen, kvSeqLen); no mask tensor exists.
+//
+// Shape of one workgroup (256 threads = 4 waves of 64):
+//   * each wave owns 32 query rows of one head; the heads of one KV group share
+//     the workgroup when the group is larger than one head, so every K/V tile
+//     staged in LDS serves all of them;
+//   * keys stream in tiles of 64: K and V rows are gathered through blockTables
+//     with 16-byte coalesced loads (one 256-byte row segment per 16 lanes),
+//     double-buffered in LDS; the loads of tile t+1 are in flight while tile t
+//     is computed;
+//   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA: K rows
+//     come from LDS, Q^T stays in registers for the whole loop.  The fp32 S^T
+//     accumulator of a lane holds 32 keys of one query row -- exactly the
+//     B-operand layout of the next MFMA, O^T += V^T P^T, so P never leaves
+//     registers; V^T comes from the row-major V tile through the LDS transpose
+//     read;
+//   * per tile a wave-uniform test decides whether a tile is fully visible for
+//     all 32 rows (no predicate), partly visible (per-element predicate) or not
+//     visible (skipped); the ALiBi bias is one or two FMAs per score; the row
+//     max and sum need one cross-half permlane swap per row;
+//   * softmax runs in the log2 domain (scale and slopes pre-multiplied by
+//     log2 e) with fp32 running max / sum; P is rounded to the input type for
+//     the PV MFMA.
+
+#include "device.h"
+#include "kernels.h"
+
+namespace mpa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kBN = 64;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
+  using V8 = typename Vec<T>::x8;
+  using V4 = typename Vec<T>::x4;
+  constexpr int KSTR = D + 8;   // K tile row stride (elements): conflict-free 16-byte row reads
+  constexpr int VSTR = D + 32;  // V tile row stride: conflict-free transpose reads
+  constexpr bool kCausal = MASK != 0;
+  constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
+  constexpr bool kAlibiSqrt = MASK == 4;
+  constexpr int NC = D / 16;                // 16-wide contraction chunks of QK^T
+  constexpr int NDT = D / 32;               // 32-row tiles of O^T
+  constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+  constexpr int CPT = kBN * CPR / 256;      // chunks per thread per tile
+
+  __shared__ __attribute__((aligned(16))) T k_lds[2][kBN * KSTR];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][kBN * VSTR];
+
+  const int4 item = p.items[blockIdx.x];
+  const int b = item.x;
+  if (b < 0) return;
+  const int head0 = item.y;
+  const int row0 = item.z;
+  const int4 sq = p.seqs[b];
+  const int L = sq.x;
+  const int kv = sq.y;
+  const long long qs = (long long)(unsigned)sq.z | ((long long)sq.w << 32);
+  const int prefix = kv - L;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int g = l >> 5;   // which half of the wave
+  const int lq = l & 31;  // query column of this lane
+  const int hpw = p.heads_per_item;
+  const int head = head0 + (w % hpw);
+  const int wrow0 = row0 + (w / hpw) * kRowsPerWave;
+  const int rows_per_item = kRowsPerWave * kWaves / hpw;
+  const int kvh = head0 / (p.head_num / p.kv_head_num);
+  const long long q_row_stride = (long long)p.head_num * D;
+  const long long kv_slot_stride = (long long)p.kv_head_num * D;
+
+  // Keys the workgroup visits, keys this wave needs, and keys every row of the
+  // wave sees (tiles below that need no predicate).
+  const int item_rows_end = min(L, row0 + rows_per_item);
+  const int wg_keys = kCausal ? min(kv, prefix + item_rows_end) : kv;
+  const int n_tiles = (wg_keys + kBN - 1) / kBN;
+  const bool w_active = wrow0 < L;
+  const int w_rows_end = min(L, wrow0 + kRowsPerWave);
+  const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
+  const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+
+  // Q^T operand: lane l holds query row wrow0 + lq, dims 16c + 8g .. +8.
+  V8 qreg[NC];
+  {
+    const int qi = wrow0 + lq;
+    const T* qrow = (const T*)p.q + (qs + qi) * q_row_stride + (long long)head * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (qi < L) {
+        qreg[c] = *(const V8*)(qrow + 16 * c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
+      }
+    }
+  }
+
+  const T* kbase = (const T*)p.k + (long long)kvh * D;
+  const T* vbase = (const T*)p.v + (long long)kvh * D;
+  const int32_t* btab = p.block_tables + (long long)b * p.max_blocks;
+  uint4 kr[CPT], vr[CPT];
+
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int x = tid + 256 * i;
+      const int row = x / CPR;
+      const int c = x % CPR;
+      const int j = j0 + row;
+      if (j < kv) {
+        int bi, slot;
+        if (p.bs_shift >= 0) {
+          bi = j >> p.bs_shift;
+          slot = j & (p.block_size - 1);
+        } else {
+          bi = j / p.block_size;
+          slot = j - bi * p.block_size;
+        }
+        const long long blk = btab[bi];
+        const long long off = (blk * p.block_size + slot) * kv_slot_stride + 8 * c;
+        kr[i] = *(const uint4*)(kbase + off);
+        vr[i] = *(const uint4*)(vbase + off);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int x = tid + 256 * i;
+      const int row = x / CPR;
+      const int c = x % CPR;
+      *(uint4*)&k_lds[buf][row * KSTR + 8 * c] = kr[i];
+      *(uint4*)&v_lds[buf][row * VSTR + 8 * c] = vr[i];
+    }
+  };
+
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;  // running max (log2 domain) of this lane's query row
+  float l_run = 0.0f;       // running sum of this lane's half of the keys
+  const int a_lane = prefix + wrow0 + lq;  // absolute position of the query row
+  float slope2 = 0.0f;
+  if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
+  const float scale2 = p.scale2;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * kBN;
+    if (t + 1 < n_tiles) load_tile(j0 + kBN);
+
+    if (w_active && j0 < w_keys) {
+      // S^T = K Q^T for keys j0 .. j0+63 (two 32-key blocks).
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const V8 a = *(const V8*)&k_lds[buf][(32 * kb + lq) * KSTR + 16 * c + 8 * g];
+          s[kb] = mfma32(a, qreg[c], s[kb]);
+        }
+      }
+      // Element (kb, r) is key j0 + 4g + C with C = 32kb + 8(r/4) + r%4.
+      const int dbase = a_lane - j0 - 4 * g;  // a - key at C = 0
+      const int klim = kv - j0 - 4 * g;       // key < kv  <=>  C < klim
+      const int vlim = kCausal ? min(klim, dbase + 1) : klim;
+      const bool partial = j0 + kBN > w_full_keys;
+      const float nb = -slope2 * (float)dbase;
+      const float dbf = (float)dbase;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
+          float x;
+          if constexpr (kAlibiLinear) {
+            x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nb));
+          } else if constexpr (kAlibiSqrt) {
+            x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), s[kb][r] * scale2);
+          } else {
+            x = s[kb][r] * scale2;
+          }
+          if (partial) x = (C < vlim) ? x : -INFINITY;
+          s[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = max_with_other_half(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(s[kb][r] - m_use);
+          s[kb][r] = e;
+          psum += e;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+
+      // O^T += V^T P^T, 16 keys per MFMA.  P^T operand of key chunk kc: registers
+      // 8(kc%2) .. +8 of S^T block kc/2, i.e. keys 16kc + {4g..4g+3, 8+4g..8+4g+3}.
+      V8 pk[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[kc][e] = (T)s[kc >> 1][8 * (kc & 1) + e];
+      }
+      const int tr_row = 4 * g + ((l & 15) >> 2);
+      const int tr_col = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const T* src = &v_lds[buf][(16 * kc + tr_row) * VSTR + 32 * dt + tr_col];
+          const s16x4 lo = lds_read_tr16(src);
+          const s16x4 hi = lds_read_tr16(src + 8 * VSTR);
+          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = mfma32(__builtin_bit_cast(V8, both), pk[kc], o[dt]);
+        }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!w_active) return;
+  const float l_tot = sum_with_other_half(l_run);
+  const int i = wrow0 + lq;
+  if (i >= L) return;
+  const float inv = 1.0f / l_tot;
+  T* orow = (T*)p.out + (qs + i) * q_row_stride + (long long)head * D + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      V4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * rg + e] * inv);
+      *(V4*)(orow + 32 * dt + 8 * rg) = v;
+    }
+  }
+  if (p.lse != nullptr && g == 0) {
+    float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if constexpr (MASK == 5) lse += p.slopes[head] * (float)a_lane;
+    p.lse[(qs + i) * p.head_num + head] = lse;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
+  const dim3 g(grid), blk(256);
+  switch (mask_type) {
+    case 0: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 0>), g, blk, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 3>), g, blk, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 4>), g, blk, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 5>), g, blk, 0, s, p); break;
+    case 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 9>), g, blk, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
+                          int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (dtype == 0) {
+    return head_size == 64 ? launch_mask<_Float16, 64>(p, mask_type, grid, stream)
+                           : launch_mask<_Float16, 128>(p, mask_type, grid, stream);
+  }
+  return head_size == 64 ? launch_mask<__bf16, 64>(p, mask_type, grid, stream)
+                         : launch_mask<__bf16, 128>(p, mask_type, grid, stream);
+}
+
+}  // namespace mpa

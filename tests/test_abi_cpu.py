@@ -1,0 +1,242 @@
+"""CPU tests of the C ABI: exported symbols, constants, argument validation (which
+runs before any HIP call) and the host launch planners.  No kernel runs here."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from masked_paged_attention_amd._lib import LIB
+    return LIB
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpa[A-Z]\w*)\s*\(", text)))
+
+
+def _header_defines():
+    out = {}
+    for name, val in re.findall(r"#define\s+(MPA_\w+)\s+(-?\d+)", open(HEADER).read()):
+        out[name] = int(val)
+    return out
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/mpa.h but not exported"
+    from masked_paged_attention_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == names
+
+
+def test_constants_match_pages():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "atb_constants.json")))
+    d = _header_defines()
+    m = g["prefix_encoder_mask_types"]
+    assert d["MPA_MASK_ALIBI_COMPRESS"] == m["MASK_TYPE_ALIBI_COMPRESS"]
+    assert d["MPA_MASK_ALIBI_COMPRESS_SQRT"] == m["MASK_TYPE_ALIBI_COMPRESS_SQRT"]
+    assert d["MPA_MASK_ALIBI_COMPRESS_LEFT_ALIGN"] == m["MASK_TYPE_ALIBI_COMPRESS_LEFT_ALIGN"]
+    assert d["MPA_MASK_CAUSAL"] == m["MASK_TYPE_CAUSAL_MASK"]
+    assert d["MPA_MLA_CALC_UNDEFINED"] == g["mla"]["CALC_TYPE_UNDEFINED"]
+    assert d["MPA_MLA_CACHE_KVCACHE"] == g["mla"]["KVCACHE"]
+    import masked_paged_attention_amd as mpa
+    assert (mpa.MASK_ALIBI, mpa.MASK_ALIBI_SQRT, mpa.MASK_ALIBI_LEFT, mpa.MASK_CAUSAL) == (3, 4, 5, 9)
+
+
+def test_error_strings(lib):
+    for s in range(5):
+        assert lib.mpaGetErrorString(s)
+    assert lib.mpaGetErrorString(99) == b"unknown status"
+    assert lib.mpaDestroyOperation(None) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _prefill(lib, **kw):
+    args = dict(query=FAKE, key=FAKE, value=FAKE, bt=FAKE, seq=[4, 7], kv=[4, 9], slopes=None,
+                mask=9, H=4, KVH=2, scale=0.125, batch=2, D=64, nb=8, bs=16, maxb=2, dtype=0,
+                qstart=None, ntok=11, out=FAKE, lse=None)
+    args.update(kw)
+    seq, ps = _i32(args["seq"]) if args["seq"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
+    kv, pk = _i32(args["kv"]) if args["kv"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
+    if args["qstart"] is not None:
+        qs = np.ascontiguousarray(np.asarray(args["qstart"], dtype=np.int64))
+        pq = qs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        pq = ctypes.POINTER(ctypes.c_int64)()
+    ws = ctypes.c_uint64(123)
+    op = ctypes.c_void_p(0xdead)
+    st = lib.mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
+        args["query"], args["key"], args["value"], args["bt"], ps, pk, args["slopes"], args["mask"],
+        args["H"], args["KVH"], args["scale"], args["batch"], args["D"], args["nb"], args["bs"],
+        args["maxb"], args["dtype"], pq, args["ntok"], args["out"], args["lse"],
+        ctypes.byref(ws), ctypes.byref(op))
+    return st, op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(query=None), 1),
+    (dict(out=None), 1),
+    (dict(bt=None), 1),
+    (dict(seq=None), 1),
+    (dict(H=0), 1),
+    (dict(KVH=3), 1),
+    (dict(KVH=0), 1),
+    (dict(dtype=2), 1),
+    (dict(mask=7), 2),
+    (dict(mask=3), 1),                  # ALiBi without slopes
+    (dict(slopes=FAKE), 1),             # slopes with causal
+    (dict(D=96), 2),
+    (dict(seq=[5, 7], kv=[4, 9]), 1),   # kvSeqLen < seqLen
+    (dict(seq=[-1, 7]), 1),
+    (dict(kv=[4, 40]), 1),              # needs 3 blocks > maxBlockNum 2
+    (dict(ntok=10), 1),                 # rows exceed nTokens
+    (dict(qstart=[0, 2], ntok=20), 1),  # overlapping padded rows
+    (dict(batch=0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(bs=0), 1),
+])
+def test_prefill_validation(lib, kw, status):
+    st, op = _prefill(lib, **kw)
+    assert st == status, lib.mpaGetLastErrorMessage()
+    assert op.value is None or op.value == 0
+    assert lib.mpaGetLastErrorMessage()
+
+
+def test_prefill_valid_args_reach_hip_or_succeed(lib):
+    st, op = _prefill(lib)
+    # With no GPU the first HIP call fails; with a GPU phase 1 succeeds (no kernel runs).
+    assert st in (0, 4), lib.mpaGetLastErrorMessage()
+    if st == 0:
+        assert lib.mpaDestroyOperation(op) == 0
+
+
+def _mla(lib, **kw):
+    args = dict(qn=FAKE, qr=FAKE, ckv=FAKE, kr=FAKE, bt=FAKE, ctx=[100, 300], ql=None, H=16,
+                scale=0.07, KVH=1, mask=0, calc=0, cache=1, batch=2, nb=8, bs=64, maxb=5, dtype=1,
+                out=FAKE, lse=None)
+    args.update(kw)
+    ctx, pc = _i32(args["ctx"]) if args["ctx"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
+    ql, pq = _i32(args["ql"]) if args["ql"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
+    ws = ctypes.c_uint64(0)
+    op = ctypes.c_void_p(0)
+    st = lib.mpaMLAGetWorkspaceSize(args["qn"], args["qr"], args["ckv"], args["kr"], args["bt"], pc, pq,
+                                    args["H"], args["scale"], args["KVH"], args["mask"], args["calc"],
+                                    args["cache"], args["batch"], args["nb"], args["bs"], args["maxb"],
+                                    args["dtype"], args["out"], args["lse"], ctypes.byref(ws),
+                                    ctypes.byref(op))
+    return st, op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qn=None), 1),
+    (dict(ctx=None), 1),
+    (dict(KVH=2), 2),
+    (dict(cache=2), 2),
+    (dict(cache=3), 2),
+    (dict(calc=2), 2),                   # RING
+    (dict(calc=3), 2),                   # PREFILL
+    (dict(mask=2), 2),                   # MASK_FREE
+    (dict(calc=1), 1),                   # SPEC without qSeqLen
+    (dict(ql=[1, 1]), 1),                # qSeqLen without SPEC
+    (dict(calc=1, ql=[0, 2]), 1),
+    (dict(calc=1, ql=[101, 2]), 1),      # more tokens than keys
+    (dict(kr=None), 1),                  # cacheMode 1 needs kRope
+    (dict(cache=0), 1),                  # cacheMode 0 with kRope
+    (dict(ctx=[0, 5]), 1),
+    (dict(ctx=[100, 400]), 1),           # 7 blocks > maxBlockNum 5
+    (dict(H=0), 1),
+    (dict(dtype=5), 1),
+])
+def test_mla_validation(lib, kw, status):
+    st, op = _mla(lib, **kw)
+    assert st == status, lib.mpaGetLastErrorMessage()
+    assert op.value is None or op.value == 0
+
+
+def test_mla_execute_rejects_small_workspace_and_wrong_op(lib):
+    assert lib.mpaMLA(None, 0, None, None) == 1
+    assert lib.mpaSelfAttentionPrefixEncoder(None, 0, None, None) == 1
+
+
+# ---------------------------------------------------------------------------
+# Planners (host only).
+# ---------------------------------------------------------------------------
+
+def _visible_keys(kv, L, i, causal):
+    return min(kv, kv - L + i + 1) if causal else kv
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_plan_covers_every_row_once(seed):
+    import masked_paged_attention_amd as mpa
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 7))
+    L = rng.integers(0, 600, size=B)
+    P = rng.integers(0, 900, size=B)
+    H, KVH = [(4, 4), (8, 2), (32, 8), (6, 2), (12, 3), (16, 1)][seed]
+    mask = [9, 0, 3, 9, 4, 5][seed]
+    causal = mask != 0
+    items, rows, keys, hpi = mpa.plan_prefill(L, L + P, mask, H, KVH)
+    assert keys == 64 and rows * hpi == 128
+    seen = {}
+    group_xcd = {}
+    for pos, (b, h0, r0, nt) in enumerate(items):
+        if b < 0:
+            continue
+        for h in range(h0, h0 + hpi):
+            assert h // (H // KVH) == h0 // (H // KVH), "a workgroup mixes KV heads"
+            for i in range(r0, min(r0 + rows, L[b])):
+                seen[(b, h, i)] = seen.get((b, h, i), 0) + 1
+        last = min(r0 + rows, L[b]) - 1
+        want = -(-_visible_keys(L[b] + P[b], L[b], last, causal) // 64)
+        assert nt == want
+        key = (b, h0 // (H // KVH))
+        group_xcd.setdefault(key, set()).add(pos % 8)
+    expect = {(b, h, i) for b in range(B) for h in range(H) for i in range(L[b])}
+    assert set(seen) == expect
+    assert all(v == 1 for v in seen.values())
+    # every (sequence, KV head) group lands on one XCD (workgroup id mod 8)
+    assert all(len(x) == 1 for x in group_xcd.values())
+
+
+@pytest.mark.parametrize("spec", [False, True])
+def test_mla_plan_splits_partition_keys(spec):
+    import masked_paged_attention_amd as mpa
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(1, 9000, size=37)
+    ql = rng.integers(1, 5, size=37) if spec else None
+    splits = mpa.plan_mla(ctx, ql, 128, 1 if spec else 0)
+    assert len(splits) % 8 == 0
+    by_b = {}
+    for b, k0, k1, idx in splits:
+        if b < 0:
+            continue
+        assert k1 > k0
+        by_b.setdefault(b, []).append((k0, k1, idx))
+    for b in range(len(ctx)):
+        parts = sorted(by_b[b])
+        assert parts[0][0] == 0 and parts[-1][1] == ctx[b]
+        for (a0, a1, _), (c0, c1, _) in zip(parts, parts[1:]):
+            assert a1 == c0
+        for k0, k1, _ in parts[:-1]:
+            assert k0 % 32 == 0 and k1 % 32 == 0
+        assert sorted(i for _, _, i in parts) == list(range(len(parts)))

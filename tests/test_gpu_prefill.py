@@ -1,0 +1,145 @@
+"""GPU parity of the prefill (PrefixEncoder) kernel against the fp64 oracle, through
+the C ABI, plus GPU-side invariants.  Tolerances: max-abs 5e-3 (fp16), 2e-2
+(bf16); LSE within 1e-3 * max(1, |LSE|)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import (check_prefill_full, check_prefill_sampled, gpu_prefill, log)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(seed, seq, prefix, H, KVH, D, bs, dtype, mask, poison=True, pad_to=None, scale=None):
+    seq = np.asarray(seq)
+    kv = seq + np.asarray(prefix)
+    slopes = "alibi" if mask in (3, 4, 5) else None
+    c = W.make_prefill(seed, seq, kv, H, KVH, D, bs, dtype, mask,
+                       scale if scale is not None else 1.0 / np.sqrt(D), slopes=slopes,
+                       poison=poison, pad_to=pad_to, name=f"s{seed}-{dtype}-D{D}-m{mask}-bs{bs}")
+    return c.to(DEV)
+
+
+def test_tiny_causal_config():
+    log("case tiny_causal (batch 2, seqLen [16,37], fp16, D 64, blockSize 16)")
+    c = W.make_prefill_config("tiny_causal", poison=True, device=DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", [0, 3, 4, 5, 9])
+def test_small_all_masks(dtype, D, mask):
+    bs = {64: 16, 128: 24}[D]
+    log(f"case small dtype={dtype} D={D} mask={mask} bs={bs}")
+    c = _case(10 + mask + D, [150, 67, 1], [0, 90, 200], 4, 2, D, bs, dtype, mask)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("H,KVH", [(8, 8), (8, 4), (8, 2), (16, 2), (24, 3), (6, 1)])
+def test_gqa_ratios(H, KVH):
+    log(f"case gqa H={H} KVH={KVH}")
+    c = _case(40 + H + KVH, [300, 129], [700, 0], H, KVH, 128, 128, "bf16", 9)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+def test_padded_layout_leaves_padding_rows_untouched():
+    log("case padded layout with sentinel")
+    c = _case(51, [200, 5, 129], [30, 0, 64], 4, 4, 128, 16, "fp16", 3, pad_to=256)
+    out, lse = gpu_prefill(c, sentinel=7.0)
+    check_prefill_full(c, out, lse)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    for b, L in enumerate(c.seq_len):
+        lo, hi = 256 * b + L, 256 * (b + 1)
+        assert (o[lo:hi] == 7.0).all() and (l[lo:hi] == 7.0).all(), f"padding rows of sequence {b} written"
+
+
+def test_empty_and_tiny_sequences():
+    log("case empty / single-row sequences")
+    c = _case(53, [0, 70, 0, 1, 33], [40, 30, 0, 0, 0], 4, 4, 64, 16, "bf16", 9)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+def test_deterministic_and_paged_equals_contiguous():
+    log("case determinism + paged vs contiguous")
+    c = _case(55, [260, 190], [100, 333], 8, 2, 128, 32, "bf16", 3, poison=False)
+    o1, l1 = gpu_prefill(c)
+    o2, l2 = gpu_prefill(c)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # Same values, blocks laid out in order (identity block table).
+    bs = c.block_size
+    key = torch.zeros_like(c.key)
+    value = torch.zeros_like(c.value)
+    bt = torch.zeros_like(c.block_tables)
+    nxt = 0
+    for b in range(c.batch):
+        for blk in range(-(-int(c.kv_seq_len[b]) // bs)):
+            src = int(c.block_tables[b, blk])
+            key[nxt] = c.key[src]
+            value[nxt] = c.value[src]
+            bt[b, blk] = nxt
+            nxt += 1
+    import dataclasses
+    c2 = dataclasses.replace(c, key=key, value=value, block_tables=bt)
+    o3, l3 = gpu_prefill(c2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_left_aligned_equals_right_aligned():
+    log("case left vs right ALiBi")
+    c = _case(57, [300, 80], [0, 500], 4, 4, 128, 128, "bf16", 3, poison=False)
+    o_r, l_r = gpu_prefill(c)
+    import dataclasses
+    c5 = dataclasses.replace(c, mask_type=5)
+    o_l, l_l = gpu_prefill(c5)
+    assert torch.equal(o_r, o_l)
+    starts = c.row_starts()
+    for b in range(c.batch):
+        a = (c.kv_seq_len[b] - c.seq_len[b]) + np.arange(c.seq_len[b])
+        d = (l_l - l_r)[starts[b]:starts[b] + c.seq_len[b]].cpu().numpy()
+        want = c.slopes[None, :].astype(np.float64) * a[:, None]
+        assert np.abs(d - want).max() <= 1e-3 * max(1.0, np.abs(want).max())
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    log("case GQA vs MHA")
+    c = _case(59, [200, 90], [64, 0], 8, 2, 128, 16, "fp16", 9, poison=False)
+    o1, l1 = gpu_prefill(c)
+    import dataclasses
+    g = c.head_num // c.kv_head_num
+    c2 = dataclasses.replace(c, key=c.key.repeat_interleave(g, dim=2).contiguous(),
+                             value=c.value.repeat_interleave(g, dim=2).contiguous(),
+                             kv_head_num=c.head_num)
+    o2, l2 = gpu_prefill(c2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["prefix_gqa_causal", "alibi_right_4x4096", "alibi_sqrt_16384",
+                                  "alibi_left_16384", "alibi_sqrt_varlen16", "alibi_left_padded16"])
+def test_full_size_configs_sampled(name):
+    log(f"case full-size {name}")
+    c = W.make_prefill_config(name, poison=True, device=DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_sampled(c, out, lse, n=160, seed=1)
+
+
+def test_packed_equals_padded_full_size():
+    log("case packed vs padded (16 lognormal sequences, sqrt ALiBi)")
+    c = W.make_prefill_config("alibi_sqrt_varlen16", poison=False, device=DEV)
+    cp = W.pad_prefill_case(c, 8192, 123, poison=True, device=DEV)
+    o1, l1 = gpu_prefill(c)
+    o2, l2 = gpu_prefill(cp)
+    s1, s2 = c.row_starts(), cp.row_starts()
+    for b in range(c.batch):
+        L = int(c.seq_len[b])
+        assert torch.equal(o1[s1[b]:s1[b] + L], o2[s2[b]:s2[b] + L])
+        assert torch.equal(l1[s1[b]:s1[b] + L], l2[s2[b]:s2[b] + L])

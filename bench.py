@@ -1,0 +1,303 @@
+"""Benchmark of the masked paged-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill: the prefix-encoder causal GQA workload (batch 8, seqLen ~ U[128,1024],
+    cached prefix ~ U[0,2048], 32 query / 8 KV heads, headSize 128, blockSize 128,
+    bf16), one PrefixEncoder launch;
+  * decode: MLA on the latent paged cache (batch 64, 128 heads, q_len 1, 576/512,
+    blockSize 128, contextLens ~ U[1024,8192], bf16), split + combine, reading one
+    of two rotated KV caches (2 x 340 MB > the 256 MB Infinity Cache) so the cache
+    is cold.
+value = valid prefill FLOPs (4 * headSize per visible (query, key) pair) / prefill
+kernel time; the decode rate (algorithmic bytes / MLA call time) is reported
+beside it.  Kernel times come from HIP events recorded on the launch stream
+around each launch inside the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "valid-FLOP attention TFLOP/s + % MFMA peak (prefill); decode GB/s + % HBM"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+# ---------------------------------------------------------------------------
+# Work accounting (closed forms; pinned by tests/test_bench_accounting.py).
+# ---------------------------------------------------------------------------
+
+def visible_pairs(seq_len, kv_seq_len, causal):
+    """Visible (query row, key) pairs of one head: row i of sequence b sees
+    min(kv, kv - L + i + 1) keys when causal, kv otherwise."""
+    tot = 0
+    for L, kv in zip(seq_len, kv_seq_len):
+        L, kv = int(L), int(kv)
+        if causal:
+            P = kv - L
+            tot += L * P + L * (L + 1) // 2
+        else:
+            tot += L * kv
+    return tot
+
+
+def prefill_valid_flops(seq_len, kv_seq_len, causal, head_num, head_size):
+    """2*D for q.k plus 2*D for p*v per visible pair, every query head."""
+    return visible_pairs(seq_len, kv_seq_len, causal) * head_num * 4 * head_size
+
+
+def padding_positions(lengths, padded_to):
+    """B * Lmax - sum L_i (padding count of a padded batch)."""
+    return len(lengths) * int(padded_to) - int(np.sum(lengths))
+
+
+def mla_bytes(context_lens, q_tokens, head_num, elem=2, with_lse=True, max_blocks=None):
+    """Algorithmic HBM bytes of one MLA call: every latent row (512 + 64 values)
+    once, the query (576), the output (512), the LSE (fp32) and the block table."""
+    kv = int(np.sum(context_lens)) * 576 * elem
+    q = q_tokens * head_num * 576 * elem
+    o = q_tokens * head_num * 512 * elem
+    lse = q_tokens * head_num * 4 if with_lse else 0
+    bt = len(context_lens) * (max_blocks or 0) * 4
+    return kv + q + o + lse + bt
+
+
+def mla_flops(context_lens, q_seq_len, head_num, spec):
+    """2*576 + 2*512 flops per visible (token, key) pair per head."""
+    pairs = 0
+    for b, ctx in enumerate(context_lens):
+        ql = 1 if q_seq_len is None else int(q_seq_len[b])
+        for t in range(ql):
+            pairs += (int(ctx) - ql + t + 1) if spec else int(ctx)
+    return pairs * head_num * (2 * 576 + 2 * 512)
+
+
+# ---------------------------------------------------------------------------
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_op(torch, run, iters, warmup):
+    """Average ms of run() over iters launches, events on the current stream."""
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle, as it is, on a bounded sample of the prefill workload: whole
+    (sequence, head) pairs in a seeded order until the time budget is spent."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    c = W.make_prefill_config("prefix_gqa_causal")
+    args = c.oracle_args()
+    rng = np.random.default_rng(0)
+    pairs = [(b, h) for b in range(c.batch) for h in range(c.head_num)]
+    order = rng.permutation(len(pairs))
+    done_flops = 0
+    done = 0
+    t0 = time.perf_counter()
+    for k in order:
+        b, h = pairs[k]
+        L = int(c.seq_len[b])
+        rows = [(b, i, h) for i in range(L)]
+        oracle.prefix_encoder_rows(rows=rows, **args)
+        done_flops += prefill_valid_flops([L], [c.kv_seq_len[b]], True, 1, c.head_size)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, head) pairs of the prefix-encoder GQA "
+                      f"workload, all rows each, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import masked_paged_attention_amd as mpa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # --- prefill workload ---
+    pc = W.make_prefill_config("prefix_gqa_causal", device=dev)
+    p_out = torch.empty_like(pc.query)
+    p_lse = torch.empty((pc.n_tokens, pc.head_num), dtype=torch.float32, device=dev)
+    p_op = mpa.PrefixEncoder(pc.query, pc.key, pc.value, pc.block_tables, pc.seq_len, pc.kv_seq_len,
+                             mask_type=pc.mask_type, qk_scale=pc.qk_scale, out=p_out, lse=p_lse)
+    p_flops = prefill_valid_flops(pc.seq_len, pc.kv_seq_len, True, pc.head_num, pc.head_size)
+
+    # --- decode workload: two independent caches, rotated per step ---
+    mcs = [W.make_mla_config("mla_decode_q1", device=dev)]
+    m2 = W.make_mla_config("mla_decode_q1", device="cpu")
+    # second copy: the same values relocated to other blocks (other memory), so
+    # consecutive steps never find the previous step's KV in the Infinity Cache
+    perm = torch.randperm(m2.ct_kv.shape[0], generator=torch.Generator().manual_seed(77))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(perm.numel())
+    import dataclasses
+    m2 = dataclasses.replace(m2, ct_kv=m2.ct_kv[perm].contiguous(), k_rope=m2.k_rope[perm].contiguous(),
+                             block_tables=inv[m2.block_tables.long()].to(torch.int32))
+    mcs.append(m2.to(dev))
+    m_out = torch.empty_like(mcs[0].q_nope)
+    m_lse = torch.empty((mcs[0].n_tokens, mcs[0].head_num), dtype=torch.float32, device=dev)
+    m_ops = [mpa.MLA(m.q_nope, m.q_rope, m.ct_kv, m.k_rope, m.block_tables, m.context_lens,
+                     qk_scale=m.qk_scale, out=m_out, lse=m_lse) for m in mcs]
+    m0 = mcs[0]
+    m_bytes = mla_bytes(m0.context_lens, m0.n_tokens, m0.head_num, max_blocks=m0.max_block_num)
+    m_flops = mla_flops(m0.context_lens, None, m0.head_num, False)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        p_op.run()
+        if ev is not None:
+            ev[1].record()
+        m_ops[i % 2].run()
+        if ev is not None:
+            ev[2].record()
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t_start, t_end = _events(torch)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    p_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    m_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    p_tflops = p_flops / (p_ms * 1e-3) / 1e12
+    m_gbs = m_bytes / (m_ms * 1e-3) / 1e9
+    print(f"bench: prefill {p_ms:.4f} ms {p_tflops:.1f} TFLOP/s; decode {m_ms:.4f} ms {m_gbs:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    extra = {}
+    if not args.no_extra:
+        for name in ["alibi_right_4x4096", "alibi_sqrt_16384", "alibi_left_16384",
+                     "alibi_sqrt_varlen16", "alibi_sqrt_padded16"]:
+            print(f"bench: extra {name}", file=sys.stderr, flush=True)
+            c = W.make_prefill_config(name, device=dev)
+            sl = torch.as_tensor(c.slopes, device=dev) if c.slopes is not None else None
+            op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
+                                   mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
+                                   q_start_loc=c.q_start_loc, return_lse=True)
+            ms = time_op(torch, op.run, 10, 3)
+            fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
+            tf = fl / (ms * 1e-3) / 1e12
+            e = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)}
+            if c.q_start_loc is not None:
+                e["padding_positions"] = padding_positions(c.seq_len, 8192)
+            extra[name] = e
+            op.close()
+            del c, op
+            torch.cuda.empty_cache()
+        print("bench: extra mla_spec_q4", file=sys.stderr, flush=True)
+        m4 = W.make_mla_config("mla_spec_q4", device=dev)
+        op4 = mpa.MLA(m4.q_nope, m4.q_rope, m4.ct_kv, m4.k_rope, m4.block_tables, m4.context_lens,
+                      qk_scale=m4.qk_scale, q_seq_len=m4.q_seq_len, mask_type=m4.mask_type,
+                      return_lse=True)
+        ms = time_op(torch, op4.run, 10, 3)
+        fl = mla_flops(m4.context_lens, m4.q_seq_len, m4.head_num, True)
+        by = mla_bytes(m4.context_lens, m4.n_tokens, m4.head_num, max_blocks=m4.max_block_num)
+        extra["mla_spec_q4"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                                "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+        op4.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    res = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefix-encoder causal GQA prefill (batch 8, seqLen~U[128,1024], prefix~U[0,2048], "
+                        "32/8 heads, headSize 128, blockSize 128, bf16) + MLA decode (batch 64, 128 heads, "
+                        "q_len 1, 576/512, blockSize 128, contextLens~U[1024,8192], bf16, cold KV)",
+            "prefill_tokens": int(pc.seq_len.sum()),
+            "prefill_valid_flops": int(p_flops),
+            "decode_batch": int(m0.batch),
+            "decode_kv_keys": int(np.sum(m0.context_lens)),
+        },
+        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel<bf16,128,causal>",
+                     "achieved": round(p_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "per_launch_flops": int(p_flops), "ms": round(p_ms, 5)},
+        "decode": {"value": round(m_gbs, 1), "unit": "GB/s", "frac_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
+                   "ms": round(m_ms, 5), "bytes": int(m_bytes),
+                   "tflops": round(m_flops / (m_ms * 1e-3) / 1e12, 1),
+                   "note": "whole MLA call (split + combine kernels)"},
+        "extra": extra,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,9 @@ int shift_of(int bs) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Fixed cost of one MLA split in keys: its 64 query rows (74 KB) plus 64
+// 16-bit partial rows written and read back (128 KB), against 1152 bytes per key.
+constexpr int kMlaSplitOverheadKeys = 176;
 
 }  // namespace
 
@@ -315,7 +318,7 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 2 * cus, 32, 64);
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, cus, 32, 64, kMlaSplitOverheadKeys);
   std::vector<int32_t> seqs(4 * (size_t)batch), seqs2(4 * (size_t)batch, 0);
   for (int b = 0; b < batch; ++b) {
     seqs[4 * b + 0] = plan.seqs[b].ctx;
@@ -362,7 +365,7 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   p.batch = batch;
   p.scale2 = qkScale * kLog2e;
   o->part_o_off = 0;
-  o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 4 + 255) & ~uint64_t(255);
+  o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 2 + 255) & ~uint64_t(255);
   o->ws_bytes = o->part_lse_off + (((uint64_t)plan.part_rows * 4 + 255) & ~uint64_t(255));
   *workspaceSize = o->ws_bytes;
   *op = o;
@@ -378,7 +381,7 @@ mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void
   if (op->ws_bytes && !workspace) return fail(MPA_ERROR_INVALID_ARG, "workspace is NULL");
   if (((uintptr_t)workspace) & 255) return fail(MPA_ERROR_INVALID_ARG, "workspace must be 256-byte aligned");
   mpa::MlaParams p = op->mp;
-  p.part_o = (float*)((char*)workspace + op->part_o_off);
+  p.part_o = (char*)workspace + op->part_o_off;
   p.part_lse = (float*)((char*)workspace + op->part_lse_off);
   hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "MLA launch");
@@ -416,7 +419,7 @@ mpaStatus mpaMLAPlanInspect(const int32_t* contextLens, const int32_t* qSeqLen, 
     if (!qSeqLen) return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
     for (int b = 0; b < batch; ++b) qlen[b] = qSeqLen[b];
   }
-  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 512, 32, 64);
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 256, 32, 64, kMlaSplitOverheadKeys);
   if (nSplits) *nSplits = (int64_t)plan.splits.size();
   if (!splits || capacity < (int64_t)plan.splits.size())
     return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu splits", (long long)capacity, plan.splits.size());

@@ -56,6 +56,32 @@ __device__ __forceinline__ float sum_with_other_half(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup barrier for data exchanged through LDS by ordinary LDS stores: waits
+// for this wave's LDS operations only, so direct global->LDS loads issued
+// earlier stay in flight across it.  The memory clobber keeps the compiler from
+// moving memory operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte direct load global -> LDS (gfx950 global_load_lds_dwordx4): lane i of
+// the wave writes its 16 bytes to lds_base + 16 * i, lds_base being wave-uniform.
+// Issued through inline asm so that the compiler's wait tracking does not see an
+// asynchronous LDS write: the caller orders it with explicit vmcnt waits and
+// barriers (the LDS base is latched at issue, so M0 is restored right after).
+__device__ __forceinline__ void dma16(const void* gsrc, const void* lds_base) {
+  const unsigned m = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds_base;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(m)
+      : "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 

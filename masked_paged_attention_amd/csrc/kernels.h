@@ -40,7 +40,7 @@ struct MlaParams {
   const int4* seqs;            // per sequence: {ctx, q_len, tok0, n_splits} (first int4)
   const int4* seqs2;           // per sequence: {split0 in seq_splits, part_row0, 0, 0}
   const int32_t* seq_splits;   // split indices of each sequence
-  float* part_o;               // [part_rows, 512] fp32 workspace
+  void* part_o;                // [part_rows, 512] partial outputs (input type) in the workspace
   float* part_lse;             // [part_rows] fp32 workspace
   void* out;                   // [T, H, 512]
   float* lse;                  // [T, H] or null

@@ -86,8 +86,8 @@ PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batc
   return plan;
 }
 
-MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int target_wgs,
-                 int key_tile, int rows_per_group) {
+MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots,
+                 int key_tile, int rows_per_group, int split_overhead_keys) {
   MlaPlan plan;
   plan.rows_per_group = rows_per_group;
   int64_t total_keys = 0;
@@ -97,11 +97,29 @@ MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_n
     max_rows = std::max(max_rows, q_len[b] * head_num);
   }
   plan.row_groups = (int)ceil_div(max_rows, plan.rows_per_group);
-  // Chunk of keys per split: about target_wgs workgroups in total, a multiple of
-  // the key tile, at least one tile.
-  const int64_t split_target = std::max<int64_t>(1, target_wgs / std::max(1, plan.row_groups));
-  int64_t chunk = ceil_div(total_keys, split_target);
-  chunk = std::max<int64_t>(key_tile, ceil_div(chunk, key_tile) * key_tile);
+  // Chunk of keys per split (a multiple of the key tile).  Cost model, in keys:
+  // the work of all splits spread over `slots` concurrent workgroups, plus the
+  // longest split (the tail), where every split also pays a fixed overhead
+  // (loading its queries, writing and re-reading its fp32 partial rows).
+  const int64_t overhead = split_overhead_keys;
+  int64_t max_ctx = 1;
+  for (int b = 0; b < batch; ++b) max_ctx = std::max<int64_t>(max_ctx, ctx[b]);
+  int64_t chunk = ceil_div(max_ctx, key_tile) * key_tile;
+  double best = -1.0;
+  for (int64_t c = key_tile; c <= ceil_div(max_ctx, key_tile) * key_tile; c += key_tile) {
+    int64_t splits = 0, longest = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int64_t n = std::max<int64_t>(1, ceil_div(ctx[b], c));
+      splits += n;
+      longest = std::max<int64_t>(longest, ceil_div(ceil_div(ctx[b], n), key_tile) * key_tile);
+    }
+    const double cost = (double)(total_keys + splits * overhead) * plan.row_groups / std::max(1, slots) +
+                        (double)(longest + overhead);
+    if (best < 0 || cost < best) {
+      best = cost;
+      chunk = c;
+    }
+  }
 
   plan.seqs.resize(batch);
   int64_t part_row = 0, tok = 0;

@@ -65,11 +65,12 @@ struct MlaPlan {
   int64_t tokens = 0;
 };
 
-// Splits every sequence's keys into chunks of nearly equal size so that about
-// `target_wgs` workgroups run; chunk boundaries are multiples of the kernel's key
-// tile.  Split s of sequence b writes q_len[b] * head_num partial rows; its
-// rows are processed by row groups of `rows_per_group`.
-MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num,
-                 int target_wgs, int key_tile, int rows_per_group);
+// Splits every sequence's keys into equal chunks (multiples of the kernel's key
+// tile) whose size minimises a makespan estimate for `slots` workgroups running
+// at once, each split costing its keys plus `split_overhead_keys`.  Split s of
+// sequence b writes q_len[b] * head_num partial rows; its rows are processed by
+// row groups of `rows_per_group`.
+MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots,
+                 int key_tile, int rows_per_group, int split_overhead_keys);
 
 }  // namespace mpa

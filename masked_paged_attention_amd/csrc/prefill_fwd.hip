@@ -30,7 +30,9 @@
 //     visible (skipped); the ALiBi bias is one or two FMAs per score; the row
 //     max and sum need one cross-half permlane swap per row;
 //   * softmax runs in the log2 domain (scale and slopes pre-multiplied by
-//     log2 e) with fp32 running max / sum; P is rounded to the input type for
+//     log2 e) with fp32 running max / sum, scores formed directly relative to
+//     a reference max that only moves when a row's max grows by more than 2^8
+//     (so the output is rarely rescaled); P is rounded to the input type for
 //     the PV MFMA.
 
 #include "device.h"
@@ -45,6 +47,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
 
 template <typename T, int D, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
@@ -116,33 +119,56 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   const T* kbase = (const T*)p.k + (long long)kvh * D;
   const T* vbase = (const T*)p.v + (long long)kvh * D;
   const int32_t* btab = p.block_tables + (long long)b * p.max_blocks;
+  // A 64-key tile lies inside one cache block when the block size is a power of
+  // two >= 64: its block id is then one wave-uniform (scalar) load, fetched two
+  // tiles ahead.  Otherwise every row looks its block up, all lookups first.
+  const bool one_block = p.bs_shift >= 6;
   uint4 kr[CPT], vr[CPT];
 
-  auto load_tile = [&](int j0) {
+  auto load_tile = [&](int j0, int blk) {
+    if (one_block) {
+      const long long base = ((long long)blk * p.block_size + (j0 & (p.block_size - 1))) * kv_slot_stride;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int x = tid + 256 * i;
-      const int row = x / CPR;
-      const int c = x % CPR;
-      const int j = j0 + row;
-      if (j < kv) {
-        int bi, slot;
-        if (p.bs_shift >= 0) {
-          bi = j >> p.bs_shift;
-          slot = j & (p.block_size - 1);
+      for (int i = 0; i < CPT; ++i) {
+        const int x = tid + 256 * i;
+        const int row = x / CPR;
+        const int c = x % CPR;
+        if (j0 + row < kv) {
+          const long long off = base + row * kv_slot_stride + 8 * c;
+          kr[i] = *(const uint4*)(kbase + off);
+          vr[i] = *(const uint4*)(vbase + off);
         } else {
-          bi = j / p.block_size;
-          slot = j - bi * p.block_size;
+          kr[i] = make_uint4(0, 0, 0, 0);
+          vr[i] = make_uint4(0, 0, 0, 0);
         }
-        const long long blk = btab[bi];
-        const long long off = (blk * p.block_size + slot) * kv_slot_stride + 8 * c;
-        kr[i] = *(const uint4*)(kbase + off);
-        vr[i] = *(const uint4*)(vbase + off);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      int bid[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int j = j0 + (tid + 256 * i) / CPR;
+        bid[i] = j < kv ? btab[j / p.block_size] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int x = tid + 256 * i;
+        const int row = x / CPR;
+        const int c = x % CPR;
+        const int j = j0 + row;
+        if (j < kv) {
+          const int slot = j - (j / p.block_size) * p.block_size;
+          const long long off = ((long long)bid[i] * p.block_size + slot) * kv_slot_stride + 8 * c;
+          kr[i] = *(const uint4*)(kbase + off);
+          vr[i] = *(const uint4*)(vbase + off);
+        } else {
+          kr[i] = make_uint4(0, 0, 0, 0);
+          vr[i] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
+  };
+  auto tile_block = [&](int t) -> int {
+    return one_block ? btab[(t * kBN) >> p.bs_shift] : 0;
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -165,14 +191,18 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
   const float scale2 = p.scale2;
 
-  load_tile(0);
+  int blk_next = n_tiles > 1 ? tile_block(1) : 0;
+  load_tile(0, tile_block(0));
   store_tile(0);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const int j0 = t * kBN;
-    if (t + 1 < n_tiles) load_tile(j0 + kBN);
+    if (t + 1 < n_tiles) {
+      load_tile(j0 + kBN, blk_next);
+      if (t + 2 < n_tiles) blk_next = tile_block(t + 2);
+    }
 
     if (w_active && j0 < w_keys) {
       // S^T = K Q^T for keys j0 .. j0+63 (two 32-key blocks).
@@ -185,13 +215,16 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
           s[kb] = mfma32(a, qreg[c], s[kb]);
         }
       }
-      // Element (kb, r) is key j0 + 4g + C with C = 32kb + 8(r/4) + r%4.
+      // Element (kb, r) is key j0 + 4g + C with C = 32kb + 8(r/4) + r%4.  Scores
+      // are formed relative to the running reference max m_ref of the row (log2
+      // domain), so that the exponent needs no further subtraction.
       const int dbase = a_lane - j0 - 4 * g;  // a - key at C = 0
       const int klim = kv - j0 - 4 * g;       // key < kv  <=>  C < klim
       const int vlim = kCausal ? min(klim, dbase + 1) : klim;
       const bool partial = j0 + kBN > w_full_keys;
-      const float nb = -slope2 * (float)dbase;
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
       const float dbf = (float)dbase;
+      const float nbm = -slope2 * dbf - m_ref;  // linear ALiBi: slope2 * (C - dbase) - m_ref
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -200,35 +233,44 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
           const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
           float x;
           if constexpr (kAlibiLinear) {
-            x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nb));
+            x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
           } else if constexpr (kAlibiSqrt) {
-            x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), s[kb][r] * scale2);
+            x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
           } else {
-            x = s[kb][r] * scale2;
+            x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
           }
           if (partial) x = (C < vlim) ? x : -INFINITY;
           s[kb][r] = x;
           mx = fmaxf(mx, x);
         }
       }
-      mx = max_with_other_half(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      mx = max_with_other_half(mx);  // tile max of the row, relative to m_ref
+      // Move the reference only when a row's max grows by more than 2^8 (or on the
+      // row's first visible key): P stays <= 2^8 and the final normalisation uses
+      // the same reference, so the result is exact; the rescale of O is rare.
+      const bool need = (m_run == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(m_run, m_ref + mx);
+        const float delta = (m_new == -INFINITY) ? 0.0f : m_new - m_ref;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kb][r] - m_use);
+          const float e = fast_exp2(s[kb][r]);
           s[kb][r] = e;
           psum += e;
         }
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      l_run += psum;
 
       // O^T += V^T P^T, 16 keys per MFMA.  P^T operand of key chunk kc: registers
       // 8(kc%2) .. +8 of S^T block kc/2, i.e. keys 16kc + {4g..4g+3, 8+4g..8+4g+3}.

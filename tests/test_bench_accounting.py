@@ -1,0 +1,50 @@
+"""CPU pins of the benchmark's work accounting: the closed-form pair counts equal a
+pair-by-pair count from the oracle's visibility rule, and the padding count
+reproduces the worked example of the nalar.dev padding-mask article."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bench
+from oracle import masks as M
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_padding_example_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "padding_example.json")))
+    assert bench.padding_positions(g["lengths"], g["padded_to"]) == g["padding_positions"]
+    assert g["padded_to"] - g["lengths"][0] == g["padding_positions_of_first_sequence"]
+
+
+@pytest.mark.parametrize("mask", [M.MASK_CAUSAL, M.MASK_NONE, M.MASK_ALIBI_SQRT])
+def test_visible_pairs_match_rule(mask):
+    rng = np.random.default_rng(mask)
+    L = rng.integers(0, 50, size=5)
+    kv = L + rng.integers(0, 40, size=5)
+    count = 0
+    for Lb, kvb in zip(L, kv):
+        a = (kvb - Lb) + np.arange(Lb)[:, None]
+        j = np.arange(kvb)[None, :]
+        count += int(M.visible(mask, a, j, kvb).sum())
+    assert bench.visible_pairs(L, kv, mask != M.MASK_NONE) == count
+    assert bench.prefill_valid_flops(L, kv, mask != M.MASK_NONE, 3, 64) == count * 3 * 4 * 64
+
+
+def test_mla_accounting():
+    ctx = [10, 20]
+    assert bench.mla_flops(ctx, None, 2, False) == 30 * 2 * 2176
+    # SPEC: token t of 3 sees ctx - 3 + t + 1 keys
+    assert bench.mla_flops(ctx, [3, 3], 1, True) == ((8 + 9 + 10) + (18 + 19 + 20)) * 2176
+    assert bench.mla_bytes(ctx, 2, 4, max_blocks=3) == 30 * 1152 + 2 * 4 * (1152 + 1024 + 4) + 2 * 3 * 4
+
+
+def test_gpus_above_one_exit_with_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(GOLDEN), "..", "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -35,6 +35,8 @@
 //     (so the output is rarely rescaled); P is rounded to the input type for
 //     the PV MFMA.
 
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -225,24 +227,35 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
       const float dbf = (float)dbase;
       const float nbm = -slope2 * dbf - m_ref;  // linear ALiBi: slope2 * (C - dbase) - m_ref
-      float mx = -INFINITY;
+      // Scores of the tile; tiles every row sees entirely take the branch without
+      // the per-element predicate (a real, wave-uniform branch).
+      auto form_scores = [&](auto with_mask) __attribute__((always_inline)) -> float {
+        float m = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
-          float x;
-          if constexpr (kAlibiLinear) {
-            x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
-          } else if constexpr (kAlibiSqrt) {
-            x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
-          } else {
-            x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
+          for (int r = 0; r < 16; ++r) {
+            const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
+            float x;
+            if constexpr (kAlibiLinear) {
+              x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
+            } else if constexpr (kAlibiSqrt) {
+              x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
+            } else {
+              x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
+            }
+            if constexpr (decltype(with_mask)::value) x = (C < vlim) ? x : -INFINITY;
+            s[kb][r] = x;
+            m = fmaxf(m, x);
           }
-          if (partial) x = (C < vlim) ? x : -INFINITY;
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
         }
+        return m;
+      };
+      float mx;
+      if (partial) {
+        mx = form_scores(std::true_type{});
+      } else {
+        mx = form_scores(std::false_type{});
       }
       mx = max_with_other_half(mx);  // tile max of the row, relative to m_ref
       // Move the reference only when a row's max grows by more than 2^8 (or on the

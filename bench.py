@@ -17,7 +17,10 @@ around each launch inside the timed region.
 """
 
 import argparse
+import csv
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -83,6 +86,116 @@ def mla_flops(context_lens, q_seq_len, head_num, spec):
 
 
 # ---------------------------------------------------------------------------
+# rocprofv3 summaries (the text files under profiles/) and the HBM traffic they hold.
+# ---------------------------------------------------------------------------
+
+# Everything that decides what the kernels do on the GPU: a change to any of these
+# files invalidates hardware counters taken before it.
+KERNEL_FILES = ("masked_paged_attention_amd/csrc/prefill_fwd.hip",
+                "masked_paged_attention_amd/csrc/mla_decode.hip",
+                "masked_paged_attention_amd/csrc/device.h",
+                "masked_paged_attention_amd/csrc/kernels.h",
+                "masked_paged_attention_amd/csrc/planner.cpp",
+                "masked_paged_attention_amd/csrc/api.cpp")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
+KERNEL_KEYS = ("prefill_fwd_kernel", "mla_split_kernel", "mla_combine_kernel")
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_kernel_name(mangled):
+    """'..prefill_fwd_kernelIDF16bLi128ELi9EEE..' -> 'prefill_fwd_kernel<bf16,128,9>'."""
+    for key in KERNEL_KEYS:
+        k = mangled.find(key)
+        if k >= 0:
+            rest = mangled[k + len(key):]
+            args = []
+            if rest.startswith("I"):
+                for m in re.finditer(r"DF16b|DF16_|Li(\d+)E", rest[:40]):
+                    args.append("bf16" if m.group(0) == "DF16b" else
+                                "fp16" if m.group(0) == "DF16_" else m.group(1))
+            return key + ("<" + ",".join(args) + ">" if args else "")
+    return mangled
+
+
+def summarize_kernel_stats(stats_csv, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["# rocprofv3 kernel statistics", "# command:", "#   " + command,
+           f"# kernel sources digest: {kernel_source_digest()}", "",
+           f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}"]
+    for r in rows:
+        out.append(f"{short_kernel_name(r['Name']):44s} {int(r['Calls']):6d} "
+                   f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                   f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):7.2f}")
+    return "\n".join(out) + "\n"
+
+
+def _pmc_per_kernel(pmc_csv, counter):
+    """Per-dispatch values of one counter, grouped by short kernel name, plus the
+    value on the largest device-copy dispatch (the calibration copy)."""
+    per = {}
+    copy = (0, None)
+    for r in csv.DictReader(open(pmc_csv)):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in r["Kernel_Name"]:
+            g = int(r["Grid_Size"])
+            if g > copy[0]:
+                copy = (g, v)
+            continue
+        per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(v)
+    return per, copy[1]
+
+
+def summarize_traffic(fetch_csv, write_csv, command, copy_bytes=1 << 30):
+    """HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by
+    what the same counters read for a device copy of copy_bytes."""
+    fetch, cf = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write, cw = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    if not cf or not cw:
+        raise SystemExit("no calibration copy in the counter files (run bench.py with --calibrate-copy)")
+    ff = copy_bytes / 1024.0 / cf
+    fw = copy_bytes / 1024.0 / cw
+    out = ["# HBM traffic per dispatch from rocprofv3 hardware counters", "# commands:"]
+    out += ["#   " + c for c in command.split(" ;; ")]
+    out += [f"# calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE {cf:.1f} KiB and "
+            f"WRITE_SIZE {cw:.1f} KiB, so fetch_factor {ff:.3f}, write_factor {fw:.3f}",
+            "# bytes = (FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor) * 1024, averaged over dispatches",
+            "", f"source_digest {kernel_source_digest()}",
+            f"{'# key':30s} {'kernel':40s} {'dispatches':>10s} {'fetch_KiB_raw':>14s} {'write_KiB_raw':>14s} {'hbm_bytes':>14s}"]
+    for k in sorted(fetch):
+        f = float(np.mean(fetch[k]))
+        w = float(np.mean(write.get(k, [0.0])))
+        b = (f * ff + w * fw) * 1024.0
+        out.append(f"{'traffic':30s} {k:40s} {len(fetch[k]):10d} {f:14.1f} {w:14.1f} {b:14.0f}")
+    return "\n".join(out) + "\n"
+
+
+def read_traffic(kernel_prefix, path=TRAFFIC_SUMMARY):
+    """HBM bytes per dispatch of the first kernel whose short name starts with
+    kernel_prefix, from the committed counter summary; None when the summary is
+    missing or was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return None
+    digest = None
+    for line in open(path):
+        f = line.split()
+        if len(f) == 2 and f[0] == "source_digest":
+            digest = f[1]
+        elif len(f) == 6 and f[0] == "traffic" and f[1].startswith(kernel_prefix):
+            return int(float(f[5])) if digest == kernel_source_digest() else None
+    return None
+
+
+# ---------------------------------------------------------------------------
 
 
 def _events(torch):
@@ -137,6 +250,10 @@ def cpu_baseline(budget_s=12.0):
                       f"workload, all rows each, fp64 numpy, {dt:.1f} s"}
 
 
+def _sum_or_none(*xs):
+    return None if any(x is None for x in xs) else int(sum(xs))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +263,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM bytes per dispatch from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--command", default="", help="the profiling command(s), recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_stats:
+        sys.stdout.write(summarize_kernel_stats(args.summarize_stats, args.command))
+        return
+    if args.summarize_traffic:
+        sys.stdout.write(summarize_traffic(*args.summarize_traffic, args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -287,11 +415,13 @@ def main():
         },
         "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel<bf16,128,causal>",
                      "achieved": round(p_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": read_traffic("prefill_fwd_kernel"),
                      "per_launch_flops": int(p_flops), "ms": round(p_ms, 5)},
         "decode": {"value": round(m_gbs, 1), "unit": "GB/s", "frac_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
                    "ms": round(m_ms, 5), "bytes": int(m_bytes),
                    "tflops": round(m_flops / (m_ms * 1e-3) / 1e12, 1),
+                   "traffic": _sum_or_none(read_traffic("mla_split_kernel"), read_traffic("mla_combine_kernel")),
                    "note": "whole MLA call (split + combine kernels)"},
         "extra": extra,
         "cpu_baseline": cpu,

@@ -48,3 +48,25 @@ def test_gpus_above_one_exit_with_message():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(GOLDEN), "..", "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_short_kernel_names():
+    assert bench.short_kernel_name(
+        "_ZN3mpa12_GLOBAL__N_118prefill_fwd_kernelIDF16bLi128ELi9EEEvNS_13PrefillParamsE") == \
+        "prefill_fwd_kernel<bf16,128,9>"
+    assert bench.short_kernel_name("_ZN3mpa12_GLOBAL__N_116mla_split_kernelIDF16_EEvNS_9MlaParamsEPKi") == \
+        "mla_split_kernel<fp16>"
+
+
+def test_traffic_summary_tracks_kernel_sources(tmp_path):
+    digest = bench.kernel_source_digest()
+    good = tmp_path / "t.txt"
+    good.write_text(f"# x\nsource_digest {digest}\n"
+                    "traffic prefill_fwd_kernel<bf16,128,9> 4 10.0 20.0 40960\n")
+    assert bench.read_traffic("prefill_fwd_kernel", str(good)) == 40960
+    assert bench.read_traffic("mla_split_kernel", str(good)) is None
+    stale = tmp_path / "s.txt"
+    stale.write_text("source_digest 0000000000000000\n"
+                     "traffic prefill_fwd_kernel<bf16,128,9> 4 10.0 20.0 40960\n")
+    assert bench.read_traffic("prefill_fwd_kernel", str(stale)) is None
+    assert bench.read_traffic("prefill_fwd_kernel", str(tmp_path / "missing.txt")) is None

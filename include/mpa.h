@@ -196,9 +196,14 @@ mpaStatus mpaPrefixEncoderPlanInspect(const int32_t *seqLen, const int32_t *kvSe
                                       int32_t *keysPerTile, int32_t *headsPerItem);
 
 /*
- * Host-only inspection of the MLA split plan.  Fills splits[0 .. *nSplits) with
- * 4 int32 each: {b, first key, end key, index of this split among the splits of
- * sequence b}, in launch order.
+ * Host-only inspection of the MLA split plan (as planned for 256 compute
+ * units).  The key tiles (32 keys) of all sequences, laid end to end, are cut
+ * into pieces of near-equal tile counts; a piece's part of one sequence is a
+ * segment.  Fills splits[0 .. *nSplits) with 5 int32 per segment, in piece
+ * order: {b, first key, end key, index of the segment among those of sequence
+ * b, piece}.  A sequence with one segment gets its output written directly;
+ * the others are merged by LSE.  Returns MPA_ERROR_INVALID_ARG if capacity (in
+ * segments) is too small; *nSplits is set either way.
  */
 mpaStatus mpaMLAPlanInspect(const int32_t *contextLens, const int32_t *qSeqLen, int32_t batch,
                             int32_t headNum, int calcType, int32_t *splits, int64_t capacity,

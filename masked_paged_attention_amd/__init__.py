@@ -281,7 +281,8 @@ def plan_prefill(seq_len, kv_seq_len, mask_type, head_num, kv_head_num, head_siz
 
 
 def plan_mla(context_lens, q_seq_len, head_num, calc_type):
-    """Host-only view of the MLA split plan: splits [n, 4] int32 {b, k0, k1, index in b}."""
+    """Host-only view of the MLA split plan (for 256 compute units): segments
+    [n, 5] int32 {b, k0, k1, index among b's segments, piece}, in piece order."""
     c, pc = _host_i32(context_lens)
     if q_seq_len is not None:
         q, pq = _host_i32(q_seq_len)
@@ -290,7 +291,7 @@ def plan_mla(context_lens, q_seq_len, head_num, calc_type):
     n = ctypes.c_int64(0)
     LIB.mpaMLAPlanInspect(pc, pq, len(c), head_num, int(calc_type), ctypes.POINTER(ctypes.c_int32)(), 0,
                           ctypes.byref(n))
-    out = np.zeros((max(1, n.value), 4), dtype=np.int32)
+    out = np.zeros((max(1, n.value), 5), dtype=np.int32)
     st = LIB.mpaMLAPlanInspect(pc, pq, len(c), head_num, int(calc_type),
                                out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n))
     _check(st, "mpaMLAPlanInspect")

@@ -49,9 +49,6 @@ int shift_of(int bs) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Fixed cost of one MLA split in keys: its 64 query rows (74 KB) plus 64
-// 16-bit partial rows written and read back (128 KB), against 1152 bytes per key.
-constexpr int kMlaSplitOverheadKeys = 176;
 
 }  // namespace
 
@@ -318,24 +315,30 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, cus, 32, 64, kMlaSplitOverheadKeys);
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, cus);
+  if (plan.part_rows >= ((int64_t)1 << 31))
+    return fail(MPA_ERROR_UNSUPPORTED, "MLA plan needs %lld partial rows (limit 2^31)", (long long)plan.part_rows);
   std::vector<int32_t> seqs(4 * (size_t)batch), seqs2(4 * (size_t)batch, 0);
+  bool any_parts = false;
   for (int b = 0; b < batch; ++b) {
-    seqs[4 * b + 0] = plan.seqs[b].ctx;
-    seqs[4 * b + 1] = plan.seqs[b].q_len;
-    seqs[4 * b + 2] = plan.seqs[b].tok0;
-    seqs[4 * b + 3] = plan.seqs[b].n_splits;
-    seqs2[4 * b + 0] = plan.seqs[b].split0;
+    const mpa::MlaSeq& q = plan.seqs[b];
+    seqs[4 * b + 0] = q.ctx;
+    seqs[4 * b + 1] = q.q_len;
+    seqs[4 * b + 2] = q.tok0;
+    seqs[4 * b + 3] = q.n_parts;
+    seqs2[4 * b + 0] = q.part_row0;
+    seqs2[4 * b + 1] = q.rows;
+    any_parts = any_parts || q.n_parts > 1;
   }
   mpaOperation* o = new (std::nothrow) mpaOperation();
   if (!o) return fail(MPA_ERROR_HIP, "out of host memory");
   o->kind = mpaOperation::kMla;
   o->dtype = dtype;
   std::vector<size_t> offs;
-  mpaStatus st = upload(o, {{plan.splits.data(), plan.splits.size() * sizeof(mpa::MlaSplit)},
+  mpaStatus st = upload(o, {{plan.segs.data(), plan.segs.size() * sizeof(mpa::MlaSegment)},
+                            {plan.piece_seg.data(), plan.piece_seg.size() * 4},
                             {seqs.data(), seqs.size() * 4},
-                            {seqs2.data(), seqs2.size() * 4},
-                            {plan.seq_splits.data(), plan.seq_splits.size() * 4}},
+                            {seqs2.data(), seqs2.size() * 4}},
                         offs);
   if (st != MPA_OK) {
     delete o;
@@ -347,10 +350,10 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   p.ckv = ctKV;
   p.krope = kRope;
   p.block_tables = blockTables;
-  p.splits = (const int4*)((char*)o->dplan + offs[0]);
-  p.seqs = (const int4*)((char*)o->dplan + offs[1]);
-  p.seqs2 = (const int4*)((char*)o->dplan + offs[2]);
-  p.seq_splits = (const int32_t*)((char*)o->dplan + offs[3]);
+  p.segs = (const int4*)((char*)o->dplan + offs[0]);
+  p.piece_seg = (const int32_t*)((char*)o->dplan + offs[1]);
+  p.seqs = (const int4*)((char*)o->dplan + offs[2]);
+  p.seqs2 = (const int4*)((char*)o->dplan + offs[3]);
   p.out = attenOut;
   p.lse = lse;
   p.head_num = headNum;
@@ -359,10 +362,12 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   p.max_blocks = maxBlockNum;
   p.ckv_stride = cacheMode == MPA_MLA_CACHE_KVCACHE ? 576 : 512;
   p.spec_mask = maskType == MPA_MLA_MASK_SPEC ? 1 : 0;
-  p.n_splits = (int)plan.splits.size();
+  p.grid = plan.grid;
   p.row_groups = plan.row_groups;
-  p.tokens = (int)plan.tokens;
+  p.pieces_per_xcd = plan.pieces_per_xcd;
   p.batch = batch;
+  p.max_rows = plan.max_rows;
+  p.any_parts = any_parts ? 1 : 0;
   p.scale2 = qkScale * kLog2e;
   o->part_o_off = 0;
   o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 2 + 255) & ~uint64_t(255);
@@ -419,22 +424,20 @@ mpaStatus mpaMLAPlanInspect(const int32_t* contextLens, const int32_t* qSeqLen, 
     if (!qSeqLen) return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
     for (int b = 0; b < batch; ++b) qlen[b] = qSeqLen[b];
   }
-  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 256, 32, 64, kMlaSplitOverheadKeys);
-  if (nSplits) *nSplits = (int64_t)plan.splits.size();
-  if (!splits || capacity < (int64_t)plan.splits.size())
-    return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu splits", (long long)capacity, plan.splits.size());
-  for (size_t i = 0; i < plan.splits.size(); ++i) {
-    const mpa::MlaSplit& s = plan.splits[i];
-    int idx = -1;
-    if (s.b >= 0) {
-      const mpa::MlaSeq& q = plan.seqs[s.b];
-      for (int k = 0; k < q.n_splits; ++k)
-        if (plan.seq_splits[q.split0 + k] == (int32_t)i) idx = k;
+  mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 256);
+  if (nSplits) *nSplits = (int64_t)plan.segs.size();
+  if (!splits || capacity < (int64_t)plan.segs.size())
+    return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu segments", (long long)capacity, plan.segs.size());
+  std::vector<int32_t> seen(batch, 0);
+  for (size_t pc = 0; pc + 1 < plan.piece_seg.size(); ++pc) {
+    for (int32_t i = plan.piece_seg[pc]; i < plan.piece_seg[pc + 1]; ++i) {
+      const mpa::MlaSegment& s = plan.segs[i];
+      splits[5 * i + 0] = s.b;
+      splits[5 * i + 1] = s.k0;
+      splits[5 * i + 2] = s.k1;
+      splits[5 * i + 3] = seen[s.b]++;
+      splits[5 * i + 4] = (int32_t)pc;
     }
-    splits[4 * i + 0] = s.b;
-    splits[4 * i + 1] = s.k0;
-    splits[4 * i + 2] = s.k1;
-    splits[4 * i + 3] = idx;
   }
   return MPA_OK;
 }

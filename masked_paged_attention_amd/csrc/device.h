@@ -82,6 +82,32 @@ __device__ __forceinline__ void dma16(const void* gsrc, const void* lds_base) {
       : "memory");
 }
 
+// Same, with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
+// offset: lane i reads sbase + voffset_i and writes its 16 bytes to
+// lds_base + 16 * i.
+__device__ __forceinline__ void dma16s(const void* sbase, unsigned voffset, const void* lds_base) {
+  const unsigned m = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds_base;
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(sbase), "s"(m)
+      : "memory");
+}
+
+// Scalar load of 16 read-only bytes (a plan record) at a wave-uniform address,
+// waited for inside the same asm block.  Scalar loads never wait on vector
+// memory, so reading the plan does not drain direct loads in flight.
+__device__ __forceinline__ int4 sload_int4(const int4* ptr) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
 

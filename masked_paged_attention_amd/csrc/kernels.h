@@ -36,24 +36,26 @@ struct MlaParams {
   const void* ckv;             // [NB, BS, 1, ckv_stride] (512 or 576 wide)
   const void* krope;           // [NB, BS, 1, 64], or null when the rope part sits in ckv
   const int32_t* block_tables; // [batch, maxBlocks]
-  const int4* splits;          // {b, k0, k1, part_row}
-  const int4* seqs;            // per sequence: {ctx, q_len, tok0, n_splits} (first int4)
-  const int4* seqs2;           // per sequence: {split0 in seq_splits, part_row0, 0, 0}
-  const int32_t* seq_splits;   // split indices of each sequence
+  const int4* segs;            // {b, k0, k1, part (-1: whole sequence)}
+  const int32_t* piece_seg;    // piece p: segments [piece_seg[p], piece_seg[p + 1])
+  const int4* seqs;            // per sequence: {ctx, q_len, tok0, n_parts}
+  const int4* seqs2;           // per sequence: {part_row0, rows (q_len * H), 0, 0}
   void* part_o;                // [part_rows, 512] partial outputs (input type) in the workspace
-  float* part_lse;             // [part_rows] fp32 workspace
+  float* part_lse;             // [part_rows] fp32 log2-domain LSE in the workspace
   void* out;                   // [T, H, 512]
   float* lse;                  // [T, H] or null
   int head_num;
   int block_size;
-  int bs_shift;
+  int bs_shift;                // log2(blockSize) when a power of two, else -1
   int max_blocks;
   int ckv_stride;              // elements per cache row of ckv (512 or 576)
   int spec_mask;               // 1: token t sees keys <= ctx - q_len + t
-  int n_splits;                // grid x of the split kernel
-  int row_groups;              // grid y of the split kernel
-  int tokens;
+  int grid;                    // split-kernel workgroups
+  int row_groups;              // workgroups per piece
+  int pieces_per_xcd;
   int batch;
+  int max_rows;                // largest q_len * H (combine grid)
+  int any_parts;               // some sequence has partial results to merge
   float scale2;                // qkScale * log2(e)
 };
 

@@ -37,173 +37,225 @@ namespace {
 constexpr int kDq = 576;        // query / key width
 constexpr int kDv = 512;        // latent value width
 constexpr int kBN = 32;         // keys per tile
-constexpr int kRows = 64;       // query rows per workgroup (2 wave pairs x 32)
+constexpr int kRows = 128;      // query rows per workgroup (4 wave pairs x 32)
+constexpr int kWaves = 8;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
 
-// LDS layout of one key tile (32 latent rows): the 512-wide part as 32 rows of
-// 1024 bytes and the 64-wide rope part as 32 rows of 128 bytes, both filled by
-// direct global->LDS loads (one wave instruction = 1024 contiguous LDS bytes).
-// 16-byte chunks are XOR-swizzled inside each row so that the QK operand reads
-// (16 rows, one chunk) and the V^T transpose reads (4 rows, 4 chunks) both hit
-// 16 distinct bank groups.
-__device__ __forceinline__ int lat_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
+// LDS layout of one key tile: key k sits in row slot lat_slot(k); a slot holds
+// the 576 values of the key (latent 512, then rope 64) and 8 values of padding,
+// 1168 bytes = 73 16-byte chunks.  An odd chunk count puts slot s at a distinct
+// bank group for every s mod 16 in a given column; the slot order (a 4x4
+// transpose inside each 16-key block) puts the 4 keys of a transpose read at
+// slots 4 apart.  So the QK operand reads (16 keys, one 16-byte column) and the
+// V^T transpose reads (4 keys x 64 bytes per half wave) both hit 16 distinct
+// bank groups, and every address is one per-lane base plus an immediate offset.
+// A key's latent part is written by one direct load (64 lanes x 16 contiguous
+// bytes), its rope part by one with 8 lanes active.
+constexpr int kLatRow = kDq + 8;  // elements per key slot
+__device__ __forceinline__ int lat_slot(int k) {
+  return (k & ~15) | ((k & 15) >> 2) | ((k & 3) << 2);
+}
+// The rope part of the 128 query rows: rows of 64 values + 8 of padding (9
+// chunks, odd), read 32 rows at a time as the B operand.
+constexpr int kQRopeRow = 72;
 
-template <typename T>
-__global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaParams p,
-                                                         const int32_t* __restrict__ block_tables) {
+template <typename T, bool ONE_BLOCK>
+__global__ void __launch_bounds__(512, 1)
+    mla_split_kernel(MlaParams p, const int32_t* __restrict__ block_tables,
+                     const int4* __restrict__ segs, const int32_t* __restrict__ piece_seg,
+                     const int4* __restrict__ seqs, const int4* __restrict__ seqs2) {
   using V8 = typename Vec<T>::x8;
-  constexpr int NCH = kDq / 16 / 2;      // 18 contraction chunks per wave of a pair
-  constexpr int NDT = kDv / 32 / 2;      // 8 O^T tiles per wave of a pair
+  constexpr int NCH = kDv / 16 / 2;  // 16 register-resident contraction chunks per wave of a pair
+  constexpr int NDT = kDv / 32 / 2;  // 8 O^T tiles per wave of a pair
 
-  // Three tile buffers, each one LDS object holding the latent rows followed by
-  // the rope rows: while tile t is computed, the loads of tiles t+1 and t+2 are
-  // in flight.
-  constexpr int kBufElems = kBN * kDv + kBN * 64;
-  __shared__ __attribute__((aligned(1024))) T tb0[kBufElems];
-  __shared__ __attribute__((aligned(1024))) T tb1[kBufElems];
-  __shared__ __attribute__((aligned(1024))) T tb2[kBufElems];
-  // Partial S^T of each wave, register-major ([4 float4][64 lanes]) so that
-  // consecutive lanes touch consecutive 16-byte slots.
-  __shared__ __attribute__((aligned(16))) float4 xch[4][4 * 64];
+  // Three key-tile buffers (latent rows, then rope rows), the pairs' partial
+  // S^T exchange, and the rope part of the 128 query rows.
+  constexpr int kBufElems = kBN * kLatRow;
+  __shared__ __attribute__((aligned(1024))) T tbuf[3 * kBufElems];
+  __shared__ __attribute__((aligned(16))) float4 xch[kWaves][4 * 64];
+  __shared__ __attribute__((aligned(16))) T qrope[kRows * kQRopeRow];
 
-  // 1-D grid.  Workgroups go round-robin to the 8 XCDs by id; ids are laid out
-  // so that the row groups of one split are dispatched back to back on the same
-  // XCD: they stream the same keys at the same time and share them through L2.
-  const int rg = p.row_groups;
-  const int lin = blockIdx.x;
-  const int blk8 = lin / (8 * rg);
-  const int within = lin - blk8 * 8 * rg;
-  const int split_id = 8 * blk8 + (within & 7);
-  const int row_group = within >> 3;
-  const int4 sp = p.splits[split_id];
-  const int b = sp.x;
-  if (b < 0) return;
-  const int k0 = sp.y, k1 = sp.z, part_row = sp.w;
-  const int4 sq = p.seqs[b];
-  const int ctx = sq.x, q_len = sq.y, tok0 = sq.z;
-  const int H = p.head_num;
-  const int M = q_len * H;                  // rows of this sequence
-  const int row_base = row_group * kRows;  // first row of this workgroup
-  if (row_base >= M) return;
+  // Workgroup -> (piece, row group): workgroups go round-robin to the 8 XCDs by
+  // id; XCD x handles pieces [x * ppx, (x + 1) * ppx), the row groups of one
+  // piece side by side.
+  const int slot = blockIdx.x >> 3;
+  const int piece = (blockIdx.x & 7) * p.pieces_per_xcd + slot / p.row_groups;
+  const int rg = slot % p.row_groups;
+  const int s_beg = piece_seg[piece];
+  const int s_end = piece_seg[piece + 1];
+  const int row_base = rg * kRows;  // first row (token-major (token, head) index) of this workgroup
+  // Segments whose sequence has rows in this row group.
+  // Plan records are read with scalar loads (see sload_int4).
+  auto next_valid = [&](int s) -> int {
+    while (s < s_end && sload_int4(&seqs2[sload_int4(&segs[s]).x]).y <= row_base) ++s;
+    return s;
+  };
+  int n_total = 0;
+  for (int s = next_valid(s_beg); s < s_end; s = next_valid(s + 1)) {
+    const int4 sg = sload_int4(&segs[s]);
+    n_total += (sg.z - sg.y + kBN - 1) / kBN;
+  }
+  if (n_total == 0) return;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int pr = w >> 1;   // pair: 32 query rows
-  const int hf = w & 1;    // half: contraction dims [288hf, +288) and output dims [256hf, +256)
+  const int hf = w & 1;    // half: contraction dims (nope [256hf, +256) + rope [32hf, +32)), output dims [256hf, +256)
   const int l = tid & 63;
   const int g = l >> 5;
   const int lq = l & 31;
+  const int H = p.head_num;
+  const int m = row_base + 32 * pr + lq;  // this lane's row within its sequence
 
-  const int m = row_base + 32 * pr + lq;  // this lane's query row
-  const bool row_ok = m < M;
-  const int t_loc = row_ok ? m / H : 0;
-  const int hh = row_ok ? m % H : 0;
-  const bool w_active = row_base + 32 * pr < M;
-  // Keys this lane's row may see: [k0, lim).
-  const int lim_full = p.spec_mask ? (ctx - q_len + t_loc + 1) : ctx;
-  const int lim = min(k1, lim_full);
-  // Keys every row of the pair sees (tiles below need no predicate).
-  int w_lim_lo = k1;
-  if (p.spec_mask) w_lim_lo = min(k1, ctx - q_len + (row_base + 32 * pr) / H + 1);
-
-  // Q^T operand: row m, dims 16(18hf + c) + 8g .. +8 (qNope below 512, then qRope).
-  V8 qreg[NCH];
+  // ---- loader cursor (wave-uniform): the tile whose loads are issued next ----
+  int ls = next_valid(s_beg);
+  int lb, lj, lk1;
   {
-    const long long qrow = (long long)(tok0 + t_loc) * H + hh;
-    const T* qn = (const T*)p.q_nope + qrow * kDv + 8 * g;
-    const T* qr = (const T*)p.q_rope + qrow * 64 + 8 * g;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int cc = NCH * hf + c;
-      if (row_ok) {
-        qreg[c] = (cc < 32) ? *(const V8*)(qn + 16 * cc) : *(const V8*)(qr + 16 * (cc - 32));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
-      }
-    }
+    const int4 sg = sload_int4(&segs[ls]);
+    lb = sg.x; lj = sg.y; lk1 = sg.z;
   }
-
-  // The block table is read-only for the kernel: wave-uniform lookups become
-  // scalar loads, which do not wait for the direct loads in flight.
-  const int32_t* __restrict__ btab = block_tables + (long long)b * p.max_blocks;
-  // Splits start at multiples of the 32-key tile, so with a power-of-two block
-  // size >= 32 a tile lies inside one cache block: one wave-uniform block id per
-  // tile, fetched two tiles ahead.  Otherwise each row looks its block up.
-  const bool one_block = p.bs_shift >= 5;
-  // Issues the direct loads of the tile starting at key j0 into (lat, rope).
-  // Rows at or beyond k1 repeat row k1 - 1 (finite data; masked later).
-  auto issue_tile = [&](int j0, int blk, T* lat, T* rope) __attribute__((always_inline)) {
-    const T* rope_base = p.krope != nullptr ? (const T*)p.krope : (const T*)p.ckv + kDv;
-    const int rope_stride = p.krope != nullptr ? 64 : p.ckv_stride;
-    const int rr = 8 * w + (l >> 3);  // rope row of this lane
-    const int rc = (l & 7) ^ rope_swz(rr);
-    if (one_block) {
-      const long long base = (long long)blk * p.block_size + (j0 & (p.block_size - 1));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 8 * w + k;
-        const long long rowi = base + min(r, k1 - 1 - j0);
-        const T* src = (const T*)p.ckv + rowi * p.ckv_stride + 8 * (l ^ lat_swz(r));
-        dma16(src, lat + r * kDv);
+  // With a power-of-two block size >= 32 every tile lies inside one cache block
+  // (tiles start at multiples of 32): one wave-uniform block id per tile.
+  // Otherwise each row looks its block up.
+  auto tile_block = [&]() -> int {
+    return ONE_BLOCK ? block_tables[(long long)lb * p.max_blocks + (lj >> p.bs_shift)] : 0;
+  };
+  auto ld_advance = [&]() {
+    lj += kBN;
+    if (lj >= lk1) {
+      ls = next_valid(ls + 1);
+      if (ls < s_end) {
+        const int4 sg = sload_int4(&segs[ls]);
+        lb = sg.x; lj = sg.y; lk1 = sg.z;
       }
-      const long long rowi = base + min(rr, k1 - 1 - j0);
-      dma16(rope_base + rowi * rope_stride + 8 * rc, rope + 64 * 8 * w);
-    } else {
-      // Block lookups first (scalar for the latent rows), then the loads.
-      long long rows[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = min(j0 + 8 * w + k, k1 - 1);
-        const int bi = j / p.block_size;
-        rows[k] = (long long)btab[bi] * p.block_size + (j - bi * p.block_size);
-      }
-      const int jr = min(j0 + rr, k1 - 1);
-      const int bir = jr / p.block_size;
-      const long long rowr = (long long)btab[bir] * p.block_size + (jr - bir * p.block_size);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 8 * w + k;
-        const T* src = (const T*)p.ckv + rows[k] * p.ckv_stride + 8 * (l ^ lat_swz(r));
-        dma16(src, lat + r * kDv);
-      }
-      dma16(rope_base + rowr * rope_stride + 8 * rc, rope + 64 * 8 * w);
     }
   };
-  auto tile_block = [&](int j0) -> int { return one_block ? btab[j0 >> p.bs_shift] : 0; };
-
-  f32x16 o[NDT];
+  // Row r of the cache: latent at lat_row(r), rope at rope_row(r).
+  const bool split_rope = p.krope != nullptr;
+  auto lat_row = [&](long long r) -> const T* { return (const T*)p.ckv + r * p.ckv_stride; };
+  auto rope_row = [&](long long r) -> const T* {
+    return split_rope ? (const T*)p.krope + r * 64 : (const T*)p.ckv + r * p.ckv_stride + kDv;
+  };
+  const unsigned lane16 = 16u * (unsigned)l;
+  // Direct loads of the loader's tile into buffer `buf`: wave w fills the slots
+  // of keys 4w .. 4w+3 (latent: 64 lanes; rope: lanes 0..7).  Keys at or beyond
+  // the segment end repeat its last key (finite data, masked later).
+  auto issue_tile = [&](int blk, T* buf) __attribute__((always_inline)) {
+    const int last = lk1 - 1 - lj;
+    long long rows[4];
+    if constexpr (ONE_BLOCK) {
+      const long long base = (long long)blk * p.block_size + (lj & (p.block_size - 1));
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+      for (int k = 0; k < 4; ++k) rows[k] = base + min(4 * w + k, last);
+    } else {
+      const int32_t* bt = block_tables + (long long)lb * p.max_blocks;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = lj + min(4 * w + k, last);
+        const int bi = j / p.block_size;
+        rows[k] = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      T* slot = buf + lat_slot(4 * w + k) * kLatRow;
+      dma16s(lat_row(rows[k]), lane16, slot);
+      if (l < 8) dma16s(rope_row(rows[k]), lane16, slot + kDv);
+    }
+  };
+  // Every wave issues 8 direct loads per tile, so "s_waitcnt vmcnt(8)" waits
+  // for every tile but the most recently issued one.  (Encoding: vmcnt |
+  // expcnt 7 << 4 | lgkmcnt 15 << 8, i.e. wait on vector memory only; through
+  // the builtin so that the compiler's own wait tracking sees it.)
+  auto end_of_tile = [&](bool newer_in_flight) __attribute__((always_inline)) {
+    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | 8);
+    else __builtin_amdgcn_s_waitcnt(0xF70);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // ---- per-segment state ----
+  V8 qreg[NCH];
+  f32x16 o[NDT];
+  float m_run = -INFINITY, l_run = 0.0f;
+  bool row_ok = false, w_active = false;
+  int lim = 0, w_lim_lo = 0;
+  int cs = ls;           // compute cursor: segment, key start of the tile, segment end
+  int cj = lj, ck1 = lk1;
   const float scale2 = p.scale2;
-  const int n_tiles = (k1 - k0 + kBN - 1) / kBN;
   float4* my_x = &xch[w][l];
   const float4* other_x = &xch[w ^ 1][l];
   const int tr_row = 4 * g + ((l & 15) >> 2);
   const int tr_col = 256 * hf + 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  auto compute = [&](int t, const T* lat, const T* rope) __attribute__((always_inline)) {
-    const int j0 = k0 + t * kBN;
-    // Partial S^T (32 keys x 32 rows) over this wave's half of the 576 dims.
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // Loads the queries of the compute cursor's segment: the nope part of this
+  // lane's row into registers, the rope part of all 128 rows into LDS.
+  auto seg_begin = [&]() __attribute__((always_inline)) {
+    const int4 sg = sload_int4(&segs[cs]);
+    const int4 sq = sload_int4(&seqs[sg.x]);
+    const int4 sq2 = sload_int4(&seqs2[sg.x]);
+    const int ctx = sq.x, q_len = sq.y, tok0 = sq.z, rows = sq2.y;
+    row_ok = m < rows;
+    w_active = row_base + 32 * pr < rows;
+    const int t_loc = row_ok ? m / H : 0;
+    lim = min(sg.z, p.spec_mask ? (ctx - q_len + t_loc + 1) : ctx);
+    w_lim_lo = sg.z;
+    if (p.spec_mask) w_lim_lo = min(sg.z, ctx - q_len + (row_base + 32 * pr) / H + 1);
+    const T* qn = (const T*)p.q_nope + ((long long)tok0 * H + (row_ok ? m : 0)) * kDv + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (row_ok) {
+        qreg[c] = *(const V8*)(qn + 16 * (NCH * hf + c));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
+      }
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int r = (tid >> 3) + 64 * pass;
+      const int ch = tid & 7;
+      const int mm = row_base + r;
+      V8 v;
+      if (mm < rows) {
+        v = *(const V8*)((const T*)p.q_rope + ((long long)tok0 * H + mm) * 64 + 8 * ch);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
+      }
+      *(V8*)&qrope[r * kQRopeRow + 8 * ch] = v;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+    // The query loads complete here (behind the loads already in flight), so
+    // no later wait of the compiler's covers the direct loads issued next.
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    lds_barrier();
+  };
+
+  auto compute = [&](const T* lat) __attribute__((always_inline)) {
+    const int j0 = cj;
+    f32x16 s0 = f32x16{};
     if (w_active) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const int q16 = 2 * (NCH * hf + c) + g;  // 16-byte chunk of the 576-wide row
-        const V8 a = q16 < 64 ? *(const V8*)&lat[lq * kDv + 8 * (q16 ^ lat_swz(lq))]
-                              : *(const V8*)&rope[lq * 64 + 8 * ((q16 - 64) ^ rope_swz(lq))];
-        if (c & 1) s1 = mfma32(a, qreg[c], s1); else s0 = mfma32(a, qreg[c], s0);
+        const int q16 = 2 * (NCH * hf + c) + g;  // 16-byte chunk of the latent row
+        const V8 a = *(const V8*)&lat[lat_slot(lq) * kLatRow + 8 * q16];
+        s0 = mfma32(a, qreg[c], s0);
       }
-      s0 += s1;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int r16 = 2 * (2 * hf + c) + g;   // 16-byte chunk of the 64-wide rope part
+        const V8 a = *(const V8*)&lat[lat_slot(lq) * kLatRow + kDv + 8 * r16];
+        const V8 bq = *(const V8*)&qrope[(32 * pr + lq) * kQRopeRow + 8 * r16];
+        s0 = mfma32(a, bq, s0);
+      }
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
         my_x[16 * r] = make_float4(s0[r], s0[r + 1], s0[r + 2], s0[r + 3]);
     }
-    lds_barrier();  // the next tile's direct loads stay in flight
+    lds_barrier();  // the direct loads in flight stay in flight
     if (w_active) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
@@ -212,14 +264,13 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaParams p,
       }
       const bool partial = j0 + kBN > w_lim_lo;
       const int vlim = lim - j0 - 4 * g;  // key j0 + 4g + C visible <=> C < vlim
-      float sc[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int C = 8 * (r >> 2) + (r & 3);
         float x = s0[r] * scale2;
         if (partial) x = (C < vlim) ? x : -INFINITY;
-        sc[r] = x;
+        s0[r] = x;
         mx = fmaxf(mx, x);
       }
       mx = max_with_other_half(mx);
@@ -231,31 +282,32 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaParams p,
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         l_run *= alpha;
-        if (t > 0) {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-        }
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
       float psum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc[r] = fast_exp2(sc[r] - m_use);
-        psum += sc[r];
+        s0[r] = fast_exp2(s0[r] - m_use);
+        psum += s0[r];
       }
       l_run += psum;
-      const V8 p0 = pack8<T>(&sc[0]);
-      const V8 p1 = pack8<T>(&sc[8]);
+      V8 p0, p1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p0[e] = (T)s0[e];
+        p1[e] = (T)s0[8 + e];
+      }
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const int d = 32 * dt + tr_col;       // first of the 4 values this lane supplies
-          const int r0 = 16 * kc + tr_row;
-          const int r1 = r0 + 8;
-          const T* src0 = &lat[r0 * kDv + 8 * ((d >> 3) ^ lat_swz(r0)) + (d & 7)];
-          const T* src1 = &lat[r1 * kDv + 8 * ((d >> 3) ^ lat_swz(r1)) + (d & 7)];
+          // Keys 16kc + tr_row and the same + 8 (slot + 2), dims d .. d+3.
+          const int d = 32 * dt + tr_col;
+          const T* src0 = &lat[lat_slot(16 * kc + tr_row) * kLatRow + d];
+          const T* src1 = src0 + 2 * kLatRow;
           const s16x4 lo = lds_read_tr16(src0);
           const s16x4 hi = lds_read_tr16(src1);
           const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -265,151 +317,150 @@ __global__ void __launch_bounds__(256, 1) mla_split_kernel(MlaParams p,
     }
   };
 
-  // Each wave issues kLoadsPerTile direct loads per tile (8 latent rows + one
-  // rope block); "s_waitcnt vmcnt(kLoadsPerTile)" therefore waits for every
-  // tile but the most recently issued one.
-  auto end_of_tile = [&](bool newer_in_flight) {
-    // s_waitcnt through the builtin (encoding vmcnt | expcnt 7 << 4 | lgkmcnt
-    // 15 << 8: wait on vector memory only) so the compiler's own wait tracking
-    // sees it; the barrier itself is a memory clobber.
-    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | 9);
-    else __builtin_amdgcn_s_waitcnt(0xF70);
-    asm volatile("s_barrier" ::: "memory");
+  // Writes the segment's result: the final output (and natural-log LSE) when the
+  // segment covers the whole sequence, else the normalised partial output and
+  // its log2-domain LSE.
+  auto seg_end = [&]() __attribute__((always_inline)) {
+    if (!w_active) return;
+    const float l_tot = sum_with_other_half(l_run);
+    if (!row_ok) return;
+    const int4 sg = sload_int4(&segs[cs]);
+    const int4 sq = sload_int4(&seqs[sg.x]);
+    const int4 sq2 = sload_int4(&seqs2[sg.x]);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float lse2 = l_tot > 0.0f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    T* orow;
+    if (sg.w < 0) {
+      orow = (T*)p.out + ((long long)sq.z * H + m) * kDv;
+      if (p.lse != nullptr && g == 0 && hf == 0) p.lse[(long long)sq.z * H + m] = lse2 * kLn2;
+    } else {
+      const long long prow = (long long)sq2.x + (long long)sg.w * sq2.y + m;
+      orow = (T*)p.part_o + prow * kDv;
+      if (g == 0 && hf == 0) p.part_lse[prow] = lse2;
+    }
+    orow += 256 * hf + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        typename Vec<T>::x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * q + e] * inv);
+        *(typename Vec<T>::x4*)(orow + 32 * dt + 8 * q) = v;
+      }
+    }
   };
-  auto lat_buf = [&](auto I) -> T* {
-    if constexpr (decltype(I)::value == 0) return tb0;
-    else if constexpr (decltype(I)::value == 1) return tb1;
-    else return tb2;
-  };
-  auto rope_buf = [&](auto I) -> T* { return lat_buf(I) + kBN * kDv; };
-  std::integral_constant<int, 0> B0;
-  std::integral_constant<int, 1> B1;
-  std::integral_constant<int, 2> B2;
 
-  issue_tile(k0, tile_block(k0), tb0, tb0 + kBN * kDv);
-  if (n_tiles > 1) issue_tile(k0 + kBN, tile_block(k0 + kBN), tb1, tb1 + kBN * kDv);
-  int blk_ahead = n_tiles > 2 ? tile_block(k0 + 2 * kBN) : 0;
-  // Everything issued so far -- the query operands included -- completes here,
-  // so no load from before the loop is still pending inside it.
+  // ---- prologue: loads of the first two tiles ----
+  issue_tile(tile_block(), tbuf);
+  ld_advance();
+  if (n_total > 1) {
+    issue_tile(tile_block(), tbuf + kBufElems);
+    ld_advance();
+  }
+  int blk_next = (n_total > 2) ? tile_block() : 0;
   end_of_tile(false);
-  // One step: start the loads of tile t+2 into the buffer tile t-1 used, compute
-  // tile t, wait until tile t+1 has landed.  Unrolled by three so that every
-  // buffer is a distinct LDS object and no load forces a wait on another
-  // buffer's reads.
-  auto step = [&](int t, auto cur, auto ahead) __attribute__((always_inline)) {
-    if (t + 2 < n_tiles) {
-      issue_tile(k0 + (t + 2) * kBN, blk_ahead, lat_buf(ahead), rope_buf(ahead));
-      if (t + 3 < n_tiles) blk_ahead = tile_block(k0 + (t + 3) * kBN);
-    }
-    compute(t, lat_buf(cur), rope_buf(cur));
-    end_of_tile(t + 2 < n_tiles);
-  };
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(t, B0, B2);
-    if (t + 1 < n_tiles) step(t + 1, B1, B0);
-    if (t + 2 < n_tiles) step(t + 2, B2, B1);
-  }
+  bool first = true;  // the compute cursor sits on the first tile of a segment
 
-  if (!w_active) return;
-  const float l_tot = sum_with_other_half(l_run);
-  if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  T* orow = (T*)p.part_o + (long long)(part_row + m) * kDv + 256 * hf + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      typename Vec<T>::x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * q + e] * inv);
-      *(typename Vec<T>::x4*)(orow + 32 * dt + 8 * q) = v;
+  // ---- main loop: tile t computes from buffer t % 3 while tiles t+1 and t+2 load ----
+  for (int t = 0; t < n_total; ++t) {
+    if (first) seg_begin();
+    const int buf = t % 3;
+    if (t + 2 < n_total) {
+      issue_tile(blk_next, tbuf + ((t + 2) % 3) * kBufElems);
+      ld_advance();
+      if (t + 3 < n_total) blk_next = tile_block();
     }
-  }
-  if (g == 0 && hf == 0) {
-    p.part_lse[part_row + m] =
-        l_tot > 0.0f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    compute(tbuf + buf * kBufElems);
+    first = cj + kBN >= ck1;
+    if (first) {
+      seg_end();
+      cs = next_valid(cs + 1);
+      if (cs < s_end) {
+        const int4 sg = sload_int4(&segs[cs]);
+        cj = sg.y; ck1 = sg.z;
+      }
+    } else {
+      cj += kBN;
+    }
+    end_of_tile(t + 2 < n_total);
   }
 }
 
-// One wave per (token, head): 64 lanes x 8 values = 512.
+// Merge of a sequence's segment results: one wave per (token, head) row,
+// 64 lanes x 8 values = 512; L = log2 sum_s 2^{lse_s}, out = sum_s 2^{lse_s - L} o_s.
 template <typename T>
-__global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p) {
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  const int H = p.head_num;
-  if (wv >= p.tokens * H) return;
-  const int tok = wv / H;
-  const int h = wv % H;
-  // Sequence of this token: binary search over the token starts.
-  int lo = 0, hi = p.batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.seqs[mid].z <= tok) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int4 sq = p.seqs[b];
-  const int4 sq2 = p.seqs2[b];
+__global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int4* __restrict__ seqs,
+                                                         const int4* __restrict__ seqs2) {
+  const int b = blockIdx.y;
+  const int4 sq = seqs[b];
   const int n = sq.w;
-  const int m = (tok - sq.z) * H + h;
-  // Pass 1: the largest partial LSE (lanes fetch different splits in parallel).
+  if (n < 2) return;
+  const int4 sq2 = seqs2[b];
+  const int rows = sq2.y;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= rows) return;
+  const int l = threadIdx.x & 63;
+  const long long base = (long long)sq2.x + m;  // partial row of segment k: base + k * rows
   float mx = -INFINITY;
-  for (int k = l; k < n; k += 64) {
-    const int s = p.seq_splits[sq2.x + k];
-    mx = fmaxf(mx, p.part_lse[p.splits[s].w + m]);
-  }
+  for (int k = l; k < n; k += 64) mx = fmaxf(mx, p.part_lse[base + (long long)k * rows]);
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const float mref = (mx == -INFINITY) ? 0.0f : mx;
-  // Pass 2: weighted sum, four splits' loads in flight at a time.
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float tot = 0.0f;
-  for (int k0 = 0; k0 < n; k0 += 4) {
-    typename Vec<T>::x8 a[4];
-    float wgt[4];
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    typename Vec<T>::x8 a[8];
+    float wgt[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       if (k0 + u < n) {
-        const int s = p.seq_splits[sq2.x + k0 + u];
-        const int row = p.splits[s].w + m;
-        wgt[u] = fast_exp2(p.part_lse[row] - mref);
-        a[u] = *(const typename Vec<T>::x8*)((const T*)p.part_o + (long long)row * kDv + 8 * l);
+        const long long row = base + (long long)(k0 + u) * rows;
+        wgt[u] = p.part_lse[row];
+        a[u] = *(const typename Vec<T>::x8*)((const T*)p.part_o + row * kDv + 8 * l);
       } else {
-        wgt[u] = 0.0f;
+        wgt[u] = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[u][e] = (T)0.0f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      tot += wgt[u];
+    for (int u = 0; u < 8; ++u) {
+      const float wu = fast_exp2(wgt[u] - mref);
+      tot += wu;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wgt[u] * (float)a[u][e];
+      for (int e = 0; e < 8; ++e) acc[e] += wu * (float)a[u][e];
     }
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   typename Vec<T>::x8 v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = (T)(acc[e] * inv);
-  *(typename Vec<T>::x8*)((T*)p.out + (long long)wv * kDv + 8 * l) = v;
+  const long long orow = (long long)sq.z * p.head_num + m;
+  *(typename Vec<T>::x8*)((T*)p.out + orow * kDv + 8 * l) = v;
   if (p.lse != nullptr && l == 0) {
-    p.lse[wv] = tot > 0.0f ? (mref + __builtin_amdgcn_logf(tot)) * kLn2 : -INFINITY;
+    p.lse[orow] = tot > 0.0f ? (mref + __builtin_amdgcn_logf(tot)) * kLn2 : -INFINITY;
   }
 }
 
 template <typename T>
 hipError_t launch_typed(const MlaParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(mla_split_kernel<T>, dim3(p.n_splits * p.row_groups), dim3(256), 0, s, p,
-                     p.block_tables);
+  if (p.bs_shift >= 5)
+    hipLaunchKernelGGL((mla_split_kernel<T, true>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
+                       p.segs, p.piece_seg, p.seqs, p.seqs2);
+  else
+    hipLaunchKernelGGL((mla_split_kernel<T, false>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
+                       p.segs, p.piece_seg, p.seqs, p.seqs2);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rows = p.tokens * p.head_num;
-  hipLaunchKernelGGL(mla_combine_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, s, p);
+  if (e != hipSuccess || !p.any_parts) return e;
+  hipLaunchKernelGGL(mla_combine_kernel<T>, dim3((p.max_rows + 3) / 4, p.batch), dim3(256), 0, s, p,
+                     p.seqs, p.seqs2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream) {
-  if (p.n_splits <= 0 || p.tokens <= 0) return hipSuccess;
+  if (p.grid <= 0) return hipSuccess;
   return dtype == 0 ? launch_typed<_Float16>(p, stream) : launch_typed<__bf16>(p, stream);
 }
 

@@ -86,84 +86,67 @@ PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batc
   return plan;
 }
 
-MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots,
-                 int key_tile, int rows_per_group, int split_overhead_keys) {
+MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots) {
   MlaPlan plan;
-  plan.rows_per_group = rows_per_group;
-  int64_t total_keys = 0;
-  int max_rows = 0;
+  std::vector<int64_t> tile0(batch + 1, 0);  // first flattened tile of each sequence
   for (int b = 0; b < batch; ++b) {
-    total_keys += ctx[b];
-    max_rows = std::max(max_rows, q_len[b] * head_num);
+    tile0[b + 1] = tile0[b] + ceil_div(ctx[b], kMlaKeyTile);
+    plan.max_rows = std::max(plan.max_rows, q_len[b] * head_num);
   }
-  plan.row_groups = (int)ceil_div(max_rows, plan.rows_per_group);
-  // Chunk of keys per split (a multiple of the key tile).  Cost model, in keys:
-  // the work of all splits spread over `slots` concurrent workgroups, plus the
-  // longest split (the tail), where every split also pays a fixed overhead
-  // (loading its queries, writing and re-reading its fp32 partial rows).
-  const int64_t overhead = split_overhead_keys;
-  int64_t max_ctx = 1;
-  for (int b = 0; b < batch; ++b) max_ctx = std::max<int64_t>(max_ctx, ctx[b]);
-  int64_t chunk = ceil_div(max_ctx, key_tile) * key_tile;
-  double best = -1.0;
-  for (int64_t c = key_tile; c <= ceil_div(max_ctx, key_tile) * key_tile; c += key_tile) {
-    int64_t splits = 0, longest = 0;
-    for (int b = 0; b < batch; ++b) {
-      const int64_t n = std::max<int64_t>(1, ceil_div(ctx[b], c));
-      splits += n;
-      longest = std::max<int64_t>(longest, ceil_div(ceil_div(ctx[b], n), key_tile) * key_tile);
-    }
-    const double cost = (double)(total_keys + splits * overhead) * plan.row_groups / std::max(1, slots) +
-                        (double)(longest + overhead);
-    if (best < 0 || cost < best) {
-      best = cost;
-      chunk = c;
-    }
-  }
+  plan.row_groups = (int)ceil_div(plan.max_rows, kMlaRowsPerGroup);
+  plan.pieces_per_xcd = std::max(1, slots / (kNumXcd * plan.row_groups));
+  const int64_t total = tile0[batch];
+  // Small problems: no piece shorter than kMinTiles tiles (the rest stay empty).
+  constexpr int64_t kMinTiles = 4;
+  const int64_t n_pieces = (int64_t)kNumXcd * plan.pieces_per_xcd;
+  const int64_t used = std::max<int64_t>(1, std::min<int64_t>(n_pieces, ceil_div(total, kMinTiles)));
+  plan.grid = (int)(n_pieces * plan.row_groups);
 
   plan.seqs.resize(batch);
-  int64_t part_row = 0, tok = 0;
+  int64_t tok = 0;
   for (int b = 0; b < batch; ++b) {
-    MlaSeq s{};
+    MlaSeq& s = plan.seqs[b];
     s.ctx = ctx[b];
     s.q_len = q_len[b];
     s.tok0 = (int32_t)tok;
+    s.rows = q_len[b] * head_num;
     tok += q_len[b];
-    // Spread the keys evenly over the splits instead of leaving a short tail.
-    const int n = (int)std::max<int64_t>(1, ceil_div(ctx[b], chunk));
-    int64_t per = ceil_div(ceil_div(ctx[b], n), key_tile) * key_tile;
-    s.n_splits = 0;
-    s.split0 = -1;
-    s.part_row0 = (int32_t)part_row;
-    for (int64_t k0 = 0; k0 < ctx[b]; k0 += per) {
-      const int64_t k1 = std::min<int64_t>(ctx[b], k0 + per);
-      plan.splits.push_back({b, (int32_t)k0, (int32_t)k1, (int32_t)part_row});
-      part_row += (int64_t)q_len[b] * head_num;
-      ++s.n_splits;
-    }
-    plan.seqs[b] = s;
   }
   plan.tokens = tok;
-  plan.part_rows = part_row;
-  // Longest splits first (all are near the chunk size; short ones go last).
-  std::vector<MlaSplit> sorted = plan.splits;
-  std::stable_sort(sorted.begin(), sorted.end(), [](const MlaSplit& x, const MlaSplit& y) {
-    return (x.k1 - x.k0) > (y.k1 - y.k0);
-  });
-  plan.splits = sorted;
-  // Per sequence, the list of its splits' partial rows lives in seq_splits.
-  plan.seq_splits.clear();
-  for (int b = 0; b < batch; ++b) {
-    plan.seqs[b].split0 = (int32_t)plan.seq_splits.size();
-    int cnt = 0;
-    for (size_t i = 0; i < plan.splits.size(); ++i)
-      if (plan.splits[i].b == b) {
-        plan.seq_splits.push_back((int32_t)i);
-        ++cnt;
-      }
-    plan.seqs[b].n_splits = cnt;
+
+  // Piece p covers flattened tiles [p * total / used, (p + 1) * total / used).
+  std::vector<int32_t> n_seg(batch, 0);
+  plan.piece_seg.assign(n_pieces + 1, 0);
+  int b = 0;
+  for (int64_t p = 0; p < n_pieces; ++p) {
+    plan.piece_seg[p] = (int32_t)plan.segs.size();
+    if (p >= used) continue;
+    const int64_t a = p * total / used, e = (p + 1) * total / used;
+    while (b < batch && tile0[b + 1] <= a) ++b;
+    for (int bb = b; bb < batch && tile0[bb] < e; ++bb) {
+      const int64_t t0 = std::max(a, tile0[bb]) - tile0[bb];
+      const int64_t t1 = std::min(e, tile0[bb + 1]) - tile0[bb];
+      if (t1 <= t0) continue;
+      MlaSegment sg;
+      sg.b = bb;
+      sg.k0 = (int32_t)(t0 * kMlaKeyTile);
+      sg.k1 = (int32_t)std::min<int64_t>(ctx[bb], t1 * kMlaKeyTile);
+      sg.part = n_seg[bb]++;
+      plan.segs.push_back(sg);
+    }
   }
-  while (plan.splits.size() % kNumXcd) plan.splits.push_back({-1, 0, 0, 0});
+  plan.piece_seg[n_pieces] = (int32_t)plan.segs.size();
+  // Sequences covered by one segment write their output directly.
+  int64_t part_row = 0;
+  for (int bb = 0; bb < batch; ++bb) {
+    MlaSeq& s = plan.seqs[bb];
+    s.n_parts = n_seg[bb] > 1 ? n_seg[bb] : 0;
+    s.part_row0 = (int32_t)part_row;
+    part_row += (int64_t)s.n_parts * s.rows;
+  }
+  for (MlaSegment& sg : plan.segs)
+    if (n_seg[sg.b] == 1) sg.part = -1;
+  plan.part_rows = part_row;
   return plan;
 }
 

@@ -39,38 +39,50 @@ struct PrefillPlan {
 PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batch, bool causal,
                          int head_num, int kv_head_num);
 
-struct MlaSplit {
-  int32_t b;        // sequence, or -1 for an empty slot
-  int32_t k0, k1;   // key range [k0, k1)
-  int32_t part_row; // first row of this split's partial results in the workspace
+// MLA decode geometry: one workgroup (8 waves) covers 128 query rows -- the
+// (token, head) pairs of a sequence, token-major -- and walks key tiles of 32.
+constexpr int kMlaKeyTile = 32;
+constexpr int kMlaRowsPerGroup = 128;
+
+struct MlaSegment {
+  int32_t b;        // sequence
+  int32_t k0, k1;   // key range [k0, k1); k0 is a multiple of the key tile
+  int32_t part;     // index among the sequence's segments, or -1 when the segment
+                    // covers every key of the sequence (final output written directly)
 };
 
 struct MlaSeq {
   int32_t ctx;         // keys
   int32_t q_len;       // query tokens
   int32_t tok0;        // first token row
-  int32_t n_splits;    // splits of this sequence
-  int32_t split0;      // index (in split order) of its first split
-  int32_t part_row0;   // partial-result row of its first split
+  int32_t n_parts;     // segments of this sequence when it has more than one, else 0
+  int32_t part_row0;   // first partial-result row of its segments
+  int32_t rows;        // q_len * head_num
   int32_t pad0, pad1;
 };
 
 struct MlaPlan {
-  std::vector<MlaSplit> splits;  // padded to a multiple of kNumXcd
+  // Pieces: contiguous runs of the key tiles of all sequences (sequence after
+  // sequence), of near-equal length; piece p holds segments
+  // [piece_seg[p], piece_seg[p + 1]) of `segs`.
+  std::vector<MlaSegment> segs;
+  std::vector<int32_t> piece_seg;
   std::vector<MlaSeq> seqs;
-  std::vector<int32_t> seq_splits;  // for each sequence, its split indices (n_splits each, from split0 into this list)
-  int rows_per_group = 64;          // query rows (token, head) per workgroup
-  int row_groups = 1;               // workgroups per split along the rows
-  int64_t part_rows = 0;            // rows of fp32 partial output in the workspace
+  int row_groups = 1;          // workgroups per piece (row groups of the largest sequence)
+  int pieces_per_xcd = 1;      // pieces handled by the workgroups of one XCD
+  int grid = 8;                // workgroups: 8 * pieces_per_xcd * row_groups
+  int64_t part_rows = 0;       // partial-result rows in the workspace
   int64_t tokens = 0;
+  int max_rows = 0;            // largest q_len * head_num
 };
 
-// Splits every sequence's keys into equal chunks (multiples of the kernel's key
-// tile) whose size minimises a makespan estimate for `slots` workgroups running
-// at once, each split costing its keys plus `split_overhead_keys`.  Split s of
-// sequence b writes q_len[b] * head_num partial rows; its rows are processed by
-// row groups of `rows_per_group`.
-MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots,
-                 int key_tile, int rows_per_group, int split_overhead_keys);
+// Plans the split-KV MLA launch for `slots` workgroups resident at once (one per
+// compute unit).  The key tiles of all sequences are laid end to end and cut
+// into 8 * pieces_per_xcd pieces of near-equal tile counts; every piece is
+// processed by row_groups workgroups (one per 128-row group) that sit on one XCD,
+// and consecutive pieces go to the same XCD, so the segments of one sequence
+// mostly share an L2.  Workgroup i runs on XCD i % 8 and handles piece
+// (i % 8) * pieces_per_xcd + (i / 8) / row_groups, row group (i / 8) % row_groups.
+MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_num, int slots);
 
 }  // namespace mpa

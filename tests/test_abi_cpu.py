@@ -219,24 +219,54 @@ def test_prefill_plan_covers_every_row_once(seed):
 
 
 @pytest.mark.parametrize("spec", [False, True])
-def test_mla_plan_splits_partition_keys(spec):
+def test_mla_plan_segments_partition_keys(spec):
     import masked_paged_attention_amd as mpa
     rng = np.random.default_rng(5)
     ctx = rng.integers(1, 9000, size=37)
     ql = rng.integers(1, 5, size=37) if spec else None
-    splits = mpa.plan_mla(ctx, ql, 128, 1 if spec else 0)
-    assert len(splits) % 8 == 0
+    segs = mpa.plan_mla(ctx, ql, 128, 1 if spec else 0)
     by_b = {}
-    for b, k0, k1, idx in splits:
-        if b < 0:
-            continue
-        assert k1 > k0
-        by_b.setdefault(b, []).append((k0, k1, idx))
+    for b, k0, k1, idx, piece in segs:
+        assert 0 <= b < len(ctx) and k1 > k0
+        by_b.setdefault(b, []).append((k0, k1, idx, piece))
     for b in range(len(ctx)):
-        parts = sorted(by_b[b])
+        parts = by_b[b]
+        # in piece order, each sequence's segments are consecutive key ranges
         assert parts[0][0] == 0 and parts[-1][1] == ctx[b]
-        for (a0, a1, _), (c0, c1, _) in zip(parts, parts[1:]):
-            assert a1 == c0
-        for k0, k1, _ in parts[:-1]:
-            assert k0 % 32 == 0 and k1 % 32 == 0
-        assert sorted(i for _, _, i in parts) == list(range(len(parts)))
+        for (a0, a1, i0, p0), (c0, c1, i1, p1) in zip(parts, parts[1:]):
+            assert a1 == c0 and i1 == i0 + 1 and p1 > p0
+        for k0, k1, _, _ in parts:
+            assert k0 % 32 == 0
+        for _, k1, _, _ in parts[:-1]:
+            assert k1 % 32 == 0
+
+
+@pytest.mark.parametrize("spec", [False, True])
+def test_mla_plan_pieces_are_balanced(spec):
+    """Pieces cover the flattened 32-key tiles in order with near-equal counts:
+    256 pieces at q_len 1 (one per compute unit), 64 at q_len 4 with 128 heads
+    (4 row groups per piece)."""
+    import masked_paged_attention_amd as mpa
+    rng = np.random.default_rng(11)
+    ctx = rng.integers(1024, 8193, size=64)
+    ql = np.full(64, 4) if spec else None
+    segs = mpa.plan_mla(ctx, ql, 128, 1 if spec else 0)
+    tiles = {}
+    order = []
+    for b, k0, k1, idx, piece in segs:
+        tiles[piece] = tiles.get(piece, 0) + (k1 - k0 + 31) // 32
+        order.append((piece, b, k0))
+    assert order == sorted(order)
+    n_pieces = 64 if spec else 256
+    assert set(tiles) == set(range(n_pieces))
+    total = sum((int(c) + 31) // 32 for c in ctx)
+    assert sum(tiles.values()) == total
+    assert max(tiles.values()) - min(tiles.values()) <= 1
+
+
+def test_mla_plan_small_problem_uses_few_pieces():
+    import masked_paged_attention_amd as mpa
+    segs = mpa.plan_mla(np.array([65, 130, 9]), None, 16, 0)
+    pieces = sorted(set(int(x[4]) for x in segs))
+    assert len(pieces) == 3            # 9 tiles, at least 4 tiles per piece
+    assert all(x[1] % 32 == 0 for x in segs)

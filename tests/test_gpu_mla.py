@@ -58,3 +58,28 @@ def test_full_size_sampled(name):
                   {(0, 0), (T - 1, H - 1)})
     check_mla(c, out, lse, rows=rows)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_many_short_sequences():
+    """300 sequences of 1..40 keys: pieces hold many segments, most sequences are
+    one segment (direct output), some are cut between pieces (merged)."""
+    log("case mla 300 short sequences, 32 heads")
+    rng = np.random.default_rng(71)
+    ctx = [int(x) for x in rng.integers(1, 41, size=300)]
+    c = W.make_mla(71, ctx, None, 32, 32, "bf16", 0, 0, 1, 0.08, poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_mixed_lengths_cross_pieces(dtype):
+    """Long and short sequences side by side at 128 heads: segments cross piece
+    boundaries at arbitrary tiles; ragged tails; cacheMode 0 (rope inside ctKV)."""
+    log(f"case mla mixed lengths 128 heads {dtype}")
+    ctx = [5000, 33, 1, 4096, 127, 7777, 64, 2500]
+    c = W.make_mla(73, ctx, None, 128, 128, dtype, 0, 0, 0, 1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(5)
+    rows = sorted({(int(rng.integers(len(ctx))), int(rng.integers(128))) for _ in range(200)} |
+                  {(b, h) for b in range(len(ctx)) for h in (0, 127)})
+    check_mla(c, out, lse, rows=rows)

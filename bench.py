@@ -116,10 +116,18 @@ def short_kernel_name(mangled):
         if k >= 0:
             rest = mangled[k + len(key):]
             args = []
-            if rest.startswith("I"):
-                for m in re.finditer(r"DF16b|DF16_|Li(\d+)E", rest[:40]):
-                    args.append("bf16" if m.group(0) == "DF16b" else
-                                "fp16" if m.group(0) == "DF16_" else m.group(1))
+            if rest.startswith("I"):  # mangled template arguments
+                for m in re.finditer(r"DF16b|DF16_|Li(\d+)E|Lb([01])E", rest[:40]):
+                    t = m.group(0)
+                    args.append("bf16" if t == "DF16b" else "fp16" if t == "DF16_" else
+                                m.group(1) if m.group(1) else ("true" if m.group(2) == "1" else "false"))
+            elif rest.startswith("<"):  # demangled
+                inner = rest[1:rest.find(">")] if ">" in rest else ""
+                for a in inner.split(","):
+                    a = a.strip()
+                    # (rocprofv3 prints the mangled __bf16, DF16b, as "bool _Accum")
+                    args.append("bf16" if "bf" in a.lower() or "_Accum" in a else
+                                "fp16" if "16" in a and "float" in a.lower() else a)
             return key + ("<" + ",".join(args) + ">" if args else "")
     return mangled
 

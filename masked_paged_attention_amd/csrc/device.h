@@ -85,8 +85,7 @@ __device__ __forceinline__ void dma16(const void* gsrc, const void* lds_base) {
 // Same, with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte
 // offset: lane i reads sbase + voffset_i and writes its 16 bytes to
 // lds_base + 16 * i.
-__device__ __forceinline__ void dma16s(const void* sbase, unsigned voffset, const void* lds_base) {
-  const unsigned m = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds_base;
+__device__ __forceinline__ void dma16s_m0(const void* sbase, unsigned voffset, unsigned m) {
   unsigned saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -98,6 +97,12 @@ __device__ __forceinline__ void dma16s(const void* sbase, unsigned voffset, cons
       : "memory");
 }
 
+// Same, with the LDS destination given as a pointer.
+__device__ __forceinline__ void dma16s(const void* sbase, unsigned voffset, const void* lds_base) {
+  dma16s_m0(sbase, voffset,
+            (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds_base);
+}
+
 // Scalar load of 16 read-only bytes (a plan record) at a wave-uniform address,
 // waited for inside the same asm block.  Scalar loads never wait on vector
 // memory, so reading the plan does not drain direct loads in flight.
@@ -106,6 +111,15 @@ __device__ __forceinline__ int4 sload_int4(const int4* ptr) {
   v4i v;
   asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
   return make_int4(v[0], v[1], v[2], v[3]);
+}
+
+// Lane index 0..63 computed where it is used: the compiler cannot hoist
+// values derived from it out of a loop, so per-lane addresses needed only now
+// and then do not stay live (and occupy registers) across the loop.
+__device__ __forceinline__ int opaque_lane() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

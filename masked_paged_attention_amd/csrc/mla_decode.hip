@@ -6,23 +6,29 @@
 //   s_j = qkScale * q.k_j over keys j < contextLens (maskType SPEC: j <=
 //   contextLens - q_len + t), out = softmax(s) V, lse = ln sum_j exp(s_j).
 //
-// Kernel 1 (split): one workgroup per (key split, group of 64 query rows).
-// The rows of a sequence are its (token, head) pairs; the 4 waves form two
-// pairs, each pair owning 32 rows: one wave of a pair contracts the first 288
-// of the 576 query/key dims and accumulates output dims 0..255, the other the
-// rest; the two partial score tiles are summed through LDS.  Per tile of 32 keys the workgroup gathers the 576-wide latent
-// rows through blockTables into LDS (16-byte coalesced loads, double
-// buffered); each wave forms S^T = K Q^T with the 32x32x16 MFMA (Q^T stays in
-// registers, 36 contraction chunks), runs the online softmax in the log2 domain
-// and accumulates O^T += V^T P^T, reading V^T -- the first 512 columns of the
-// same LDS rows -- with the LDS transpose read: every latent row is loaded from
-// HBM once and serves as key and as value.  The running output is rescaled only
-// when a row's max grows by more than 2^8 (exact: the final normalisation uses
-// the same reference max).  It writes the split's normalised partial output
-// (rounded to the input type) and log2-domain LSE (fp32) to the workspace.
+// Kernel 1 (split): one workgroup of 8 waves per (piece, 128-row group), one
+// workgroup per compute unit.  The key tiles (32 keys) of all sequences, laid
+// end to end, are cut into pieces of near-equal length; a piece's part of one
+// sequence is a segment.  The rows of a sequence are its (token, head) pairs;
+// the 8 waves form 4 pairs of 32 rows: one wave of a pair contracts the first
+// half of the 576 query/key dims and accumulates output dims 0..255, the other
+// the rest; the two partial score tiles are summed through LDS.  Waves 0..3
+// gather each tile's latent rows through blockTables into LDS (direct
+// global->LDS loads, three buffers, two tiles ahead); each wave forms S^T = K
+// Q^T with the 32x32x16 MFMA (the nope part of Q^T stays in registers, the
+// rope part in LDS), runs the online softmax in the log2 domain and
+// accumulates O^T += V^T P^T, reading V^T -- the first 512 columns of the same
+// LDS rows -- with the LDS transpose read: every latent row is loaded from HBM
+// once and serves as key and as value.  Waves 0..3 and 4..7 run half a tile
+// apart so that one wave's MFMA work overlaps the other's.  The running output
+// is rescaled only when a row's max grows by more than 2^8 (exact: the final
+// normalisation uses the same reference max).  A segment that covers its whole
+// sequence writes the final output; the others write a normalised partial
+// output (rounded to the input type) and a log2-domain LSE (fp32) to the
+// workspace.
 //
-// Kernel 2 (combine): for each (token, head), LSE-weighted merge of the partials
-// of its sequence: L = log2 sum_s 2^{lse_s}, out = sum_s 2^{lse_s - L} o_s --
+// Kernel 2 (combine): for each (token, head) of a sequence with several
+// segments, LSE-weighted merge of the partials: L = log2 sum_s 2^{lse_s}, out = sum_s 2^{lse_s - L} o_s --
 // the merge by LSE that the MLA page's lse output exists for.
 
 #include <type_traits>
@@ -42,20 +48,22 @@ constexpr int kWaves = 8;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
 
-// LDS layout of one key tile: key k sits in row slot lat_slot(k); a slot holds
-// the 576 values of the key (latent 512, then rope 64) and 8 values of padding,
-// 1168 bytes = 73 16-byte chunks.  An odd chunk count puts slot s at a distinct
-// bank group for every s mod 16 in a given column; the slot order (a 4x4
-// transpose inside each 16-key block) puts the 4 keys of a transpose read at
-// slots 4 apart.  So the QK operand reads (16 keys, one 16-byte column) and the
-// V^T transpose reads (4 keys x 64 bytes per half wave) both hit 16 distinct
-// bank groups, and every address is one per-lane base plus an immediate offset.
-// A key's latent part is written by one direct load (64 lanes x 16 contiguous
-// bytes), its rope part by one with 8 lanes active.
-constexpr int kLatRow = kDq + 8;  // elements per key slot
+// LDS layout of one key tile.  Latent part: key k sits in row slot
+// lat_slot(k), 512 values + 8 of padding = 1040 bytes = 65 16-byte chunks.  An
+// odd chunk count puts slot s at a distinct bank group for every s mod 16 in a
+// given column; the slot order (a 4x4 transpose inside each 16-key block) puts
+// the 4 keys of a transpose read at slots 4 apart.  So the QK operand reads (16
+// keys, one 16-byte column) and the V^T transpose reads (4 keys x 64 bytes per
+// half wave) both hit 16 distinct bank groups, and every address is one per-lane
+// base plus an immediate offset.  A key's latent part is written by one direct
+// load (64 lanes x 16 contiguous bytes).  Rope part: 32 rows of 128 bytes after
+// the latent slots, 16-byte chunks XOR-swizzled by rope_swz (conflict-free for
+// 16 rows in one column), 8 keys per direct load.
+constexpr int kLatRow = kDv + 8;  // elements per latent slot
 __device__ __forceinline__ int lat_slot(int k) {
   return (k & ~15) | ((k & 15) >> 2) | ((k & 3) << 2);
 }
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 // The rope part of the 128 query rows: rows of 64 values + 8 of padding (9
 // chunks, odd), read 32 rows at a time as the B operand.
 constexpr int kQRopeRow = 72;
@@ -71,7 +79,8 @@ __global__ void __launch_bounds__(512, 1)
 
   // Three key-tile buffers (latent rows, then rope rows), the pairs' partial
   // S^T exchange, and the rope part of the 128 query rows.
-  constexpr int kBufElems = kBN * kLatRow;
+  constexpr int kLatElems = kBN * kLatRow;
+  constexpr int kBufElems = kLatElems + kBN * 64;
   __shared__ __attribute__((aligned(1024))) T tbuf[3 * kBufElems];
   __shared__ __attribute__((aligned(16))) float4 xch[kWaves][4 * 64];
   __shared__ __attribute__((aligned(16))) T qrope[kRows * kQRopeRow];
@@ -106,7 +115,6 @@ __global__ void __launch_bounds__(512, 1)
   const int g = l >> 5;
   const int lq = l & 31;
   const int H = p.head_num;
-  const int m = row_base + 32 * pr + lq;  // this lane's row within its sequence
 
   // ---- loader cursor (wave-uniform): the tile whose loads are issued next ----
   int ls = next_valid(s_beg);
@@ -138,41 +146,59 @@ __global__ void __launch_bounds__(512, 1)
     return split_rope ? (const T*)p.krope + r * 64 : (const T*)p.ckv + r * p.ckv_stride + kDv;
   };
   const unsigned lane16 = 16u * (unsigned)l;
-  // Direct loads of the loader's tile into buffer `buf`: wave w fills the slots
-  // of keys 4w .. 4w+3 (latent: 64 lanes; rope: lanes 0..7).  Keys at or beyond
-  // the segment end repeat its last key (finite data, masked later).
-  auto issue_tile = [&](int blk, T* buf) __attribute__((always_inline)) {
-    const int last = lk1 - 1 - lj;
-    long long rows[4];
+  // Direct loads of the loader's tile into buffer `buf`, issued by waves 0..3
+  // only: wave w fills the latent slots of keys 8w .. 8w+7 and the rope rows of
+  // the same keys.  Keys at or beyond the segment end repeat its last key
+  // (finite data, masked later).
+  const long long lat_step = (long long)p.ckv_stride * (long long)sizeof(T);
+  const long long rope_step = split_rope ? 64 * (long long)sizeof(T) : lat_step;
+  auto issue = [&](int blk, T* buf) __attribute__((always_inline)) {
+    const int last = lk1 - 1 - lj;  // last key of the segment within the tile
+    const unsigned m0buf = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)buf;
     if constexpr (ONE_BLOCK) {
-      const long long base = (long long)blk * p.block_size + (lj & (p.block_size - 1));
+      // The tile lies in one cache block: its keys are consecutive rows.
+      const long long rt = (long long)blk * p.block_size + (lj & (p.block_size - 1));
+      const char* a = (const char*)lat_row(rt + min(8 * w, last));
+      const int advances = last - 8 * w;  // rows after the first that exist
 #pragma unroll
-      for (int k = 0; k < 4; ++k) rows[k] = base + min(4 * w + k, last);
+      for (int k = 0; k < 8; ++k) {
+        dma16s_m0(a, lane16, m0buf + (unsigned)(lat_slot(8 * w + k) * kLatRow * sizeof(T)));
+        if (k < advances) a += lat_step;
+      }
+      // Rope: lane l carries key 8w + l/8 (clamped), 16-byte chunk (l % 8) ^ rope_swz(key).
+      const int ln = opaque_lane();
+      const int key = 8 * w + (ln >> 3);
+      const unsigned off = (unsigned)min(key, last) * (unsigned)rope_step +
+                           16u * (unsigned)((ln & 7) ^ rope_swz(key));
+      dma16s(rope_row(rt), off, buf + kLatElems + 64 * 8 * w);
     } else {
       const int32_t* bt = block_tables + (long long)lb * p.max_blocks;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = lj + min(4 * w + k, last);
+      for (int k = 0; k < 8; ++k) {
+        const int j = lj + min(8 * w + k, last);
         const int bi = j / p.block_size;
-        rows[k] = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
+        const long long row = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
+        dma16s_m0(lat_row(row), lane16, m0buf + (unsigned)(lat_slot(8 * w + k) * kLatRow * sizeof(T)));
       }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      T* slot = buf + lat_slot(4 * w + k) * kLatRow;
-      dma16s(lat_row(rows[k]), lane16, slot);
-      if (l < 8) dma16s(rope_row(rows[k]), lane16, slot + kDv);
+      const int ln = opaque_lane();
+      const int key = 8 * w + (ln >> 3);
+      const int j = lj + min(key, last);
+      const int bi = j / p.block_size;
+      const long long row = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
+      dma16((const char*)rope_row(row) + 16 * ((ln & 7) ^ rope_swz(key)),
+            buf + kLatElems + 64 * 8 * w);
     }
   };
-  // Every wave issues 8 direct loads per tile, so "s_waitcnt vmcnt(8)" waits
-  // for every tile but the most recently issued one.  (Encoding: vmcnt |
-  // expcnt 7 << 4 | lgkmcnt 15 << 8, i.e. wait on vector memory only; through
-  // the builtin so that the compiler's own wait tracking sees it.)
-  auto end_of_tile = [&](bool newer_in_flight) __attribute__((always_inline)) {
-    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | 8);
+  // Waves 0..3 issue 9 direct loads per tile, so "s_waitcnt vmcnt(9)" waits for
+  // every tile but the most recently issued one.  (Encoding: vmcnt | expcnt 7
+  // << 4 | lgkmcnt 15 << 8, i.e. wait on vector memory only; through the
+  // builtin so that the compiler's own wait tracking sees it.)  A loader wave
+  // waits for its own loads; the barrier after it publishes the tile to all.
+  auto wait_tiles = [&](bool newer_in_flight) __attribute__((always_inline)) {
+    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | 9);
     else __builtin_amdgcn_s_waitcnt(0xF70);
-    asm volatile("s_barrier" ::: "memory");
   };
+
   // ---- per-segment state ----
   V8 qreg[NCH];
   f32x16 o[NDT];
@@ -187,23 +213,22 @@ __global__ void __launch_bounds__(512, 1)
   const int tr_row = 4 * g + ((l & 15) >> 2);
   const int tr_col = 256 * hf + 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
-  // Loads the queries of the compute cursor's segment: the nope part of this
-  // lane's row into registers, the rope part of all 128 rows into LDS.
-  auto seg_begin = [&]() __attribute__((always_inline)) {
-    const int4 sg = sload_int4(&segs[cs]);
+  // Loads the queries of segment `seg` into this wave: the nope part of this
+  // lane's row (dims [256hf, +256)) into registers, and the rope part of the
+  // pair's 32 rows that this wave reads (dims [32hf, +32)) into LDS.  A wave
+  // writes only LDS it reads itself, so no barrier is involved.
+  auto load_q = [&](int seg) __attribute__((always_inline)) {
+    const int4 sg = sload_int4(&segs[seg]);
     const int4 sq = sload_int4(&seqs[sg.x]);
     const int4 sq2 = sload_int4(&seqs2[sg.x]);
-    const int ctx = sq.x, q_len = sq.y, tok0 = sq.z, rows = sq2.y;
-    row_ok = m < rows;
-    w_active = row_base + 32 * pr < rows;
-    const int t_loc = row_ok ? m / H : 0;
-    lim = min(sg.z, p.spec_mask ? (ctx - q_len + t_loc + 1) : ctx);
-    w_lim_lo = sg.z;
-    if (p.spec_mask) w_lim_lo = min(sg.z, ctx - q_len + (row_base + 32 * pr) / H + 1);
-    const T* qn = (const T*)p.q_nope + ((long long)tok0 * H + (row_ok ? m : 0)) * kDv + 8 * g;
+    const int tok0 = sq.z, rows = sq2.y;
+    const int ln = opaque_lane();
+    const int mm_row = row_base + 32 * pr + (ln & 31);
+    const bool ok = mm_row < rows;
+    const T* qn = (const T*)p.q_nope + ((long long)tok0 * H + (ok ? mm_row : 0)) * kDv + 8 * (ln >> 5);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if (row_ok) {
+      if (ok) {
         qreg[c] = *(const V8*)(qn + 16 * (NCH * hf + c));
       } else {
 #pragma unroll
@@ -212,8 +237,8 @@ __global__ void __launch_bounds__(512, 1)
     }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      const int r = (tid >> 3) + 64 * pass;
-      const int ch = tid & 7;
+      const int r = 32 * pr + 16 * pass + (ln >> 2);  // row within the group of 128
+      const int ch = 4 * hf + (ln & 3);               // 16-byte chunk of the 64-wide rope row
       const int mm = row_base + r;
       V8 v;
       if (mm < rows) {
@@ -224,54 +249,124 @@ __global__ void __launch_bounds__(512, 1)
       }
       *(V8*)&qrope[r * kQRopeRow + 8 * ch] = v;
     }
+    // The query loads complete here, so no later wait of the compiler's covers
+    // direct loads issued after this point.
+    __builtin_amdgcn_s_waitcnt(0xF70);
+  };
+  // Per-segment state of segment `seg`: row masks, key limits, accumulators.
+  auto reset_state = [&](int seg) __attribute__((always_inline)) {
+    const int4 sg = sload_int4(&segs[seg]);
+    const int4 sq = sload_int4(&seqs[sg.x]);
+    const int4 sq2 = sload_int4(&seqs2[sg.x]);
+    const int ctx = sq.x, q_len = sq.y, rows = sq2.y;
+    const int ln = opaque_lane();
+    const int mm_row = row_base + 32 * pr + (ln & 31);
+    row_ok = mm_row < rows;
+    w_active = row_base + 32 * pr < rows;
+    const int t_loc = row_ok ? mm_row / H : 0;
+    lim = min(sg.z, p.spec_mask ? (ctx - q_len + t_loc + 1) : ctx);
+    w_lim_lo = sg.z;
+    if (p.spec_mask) w_lim_lo = min(sg.z, ctx - q_len + (row_base + 32 * pr) / H + 1);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     m_run = -INFINITY;
     l_run = 0.0f;
-    // The query loads complete here (behind the loads already in flight), so
-    // no later wait of the compiler's covers the direct loads issued next.
-    __builtin_amdgcn_s_waitcnt(0xF70);
-    lds_barrier();
   };
 
-  auto compute = [&](const T* lat) __attribute__((always_inline)) {
-    const int j0 = cj;
+  // First half of a tile: the wave's partial S^T over its half of the 576
+  // dims, written to its exchange slot.
+  auto qk_part = [&](const T* lat) __attribute__((always_inline)) {
     f32x16 s0 = f32x16{};
+    // A operands: this lane's key row (slot), 16-byte chunks of this wave's half
+    // of the contraction: 16 latent chunks, then 2 rope chunks.  Loads run
+    // kQkDepth chunks ahead of the MFMA that consumes them.
+    const T* arow = lat + lat_slot(lq) * kLatRow;
+    auto load_a = [&](int c) -> V8 {
+      if (c < NCH) return *(const V8*)(arow + 8 * (2 * (NCH * hf + c) + g));
+      // Rope row lq, 16-byte chunk r16 (addresses recomputed here: registers).
+      const int ln = opaque_lane();
+      const int key = ln & 31;
+      const int r16 = 2 * (2 * hf + c - NCH) + (ln >> 5);
+      return *(const V8*)(lat + kLatElems + key * 64 + 8 * (r16 ^ rope_swz(key)));
+    };
+    constexpr int kQkDepth = 3;
     if (w_active) {
+      V8 ring[kQkDepth];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int q16 = 2 * (NCH * hf + c) + g;  // 16-byte chunk of the latent row
-        const V8 a = *(const V8*)&lat[lat_slot(lq) * kLatRow + 8 * q16];
-        s0 = mfma32(a, qreg[c], s0);
-      }
+      for (int c = 0; c < kQkDepth; ++c) ring[c] = load_a(c);
+      V8 bq0, bq1;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r16 = 2 * (2 * hf + c) + g;   // 16-byte chunk of the 64-wide rope part
-        const V8 a = *(const V8*)&lat[lat_slot(lq) * kLatRow + kDv + 8 * r16];
-        const V8 bq = *(const V8*)&qrope[(32 * pr + lq) * kQRopeRow + 8 * r16];
-        s0 = mfma32(a, bq, s0);
+      for (int c = 0; c < NCH + 2; ++c) {
+        const V8 a = ring[c % kQkDepth];
+        if (c + kQkDepth < NCH + 2) ring[c % kQkDepth] = load_a(c + kQkDepth);
+        if (c == NCH - 4) {
+          const T* qrow = qrope + (32 * pr + lq) * kQRopeRow + 8 * g;
+          bq0 = *(const V8*)(qrow + 8 * (4 * hf));
+          bq1 = *(const V8*)(qrow + 8 * (4 * hf + 2));
+        }
+        const V8 b = c < NCH ? qreg[c] : (c == NCH ? bq0 : bq1);
+        s0 = mfma32(a, b, s0);
+        // Keep the loads kQkDepth chunks ahead (the scheduler would otherwise
+        // sink them next to their MFMA to save registers).
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int r = 0; r < 16; r += 4)
         my_x[16 * r] = make_float4(s0[r], s0[r + 1], s0[r + 2], s0[r + 3]);
     }
-    lds_barrier();  // the direct loads in flight stay in flight
+  };
+
+  // Second half of a tile (after a barrier that made the partner's partial
+  // scores visible): full scores, online softmax, O^T += V^T P^T.
+  auto smpv_part = [&](const T* lat) __attribute__((always_inline)) {
+    const int j0 = cj;
+    f32x16 s0;
     if (w_active) {
+      // V^T operands (keys 16kc + tr_row and the same + 8, i.e. slot + 2; dims
+      // 32dt + tr_col .. +3), loaded kPvDepth MFMAs ahead; the first ones are in
+      // flight during the softmax.
+      const T* vbase = lat + lat_slot(tr_row) * kLatRow + tr_col;
+      auto load_v = [&](int i) -> V8 {
+        const T* src0 = vbase + (i >> 3) * (16 * kLatRow) + 32 * (i & 7);
+        const s16x4 lo = lds_read_tr16(src0);
+        const s16x4 hi = lds_read_tr16(src0 + 2 * kLatRow);
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kPvDepth = 2;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
+        const float4 u = my_x[16 * r];
         const float4 v = other_x[16 * r];
-        s0[r] += v.x; s0[r + 1] += v.y; s0[r + 2] += v.z; s0[r + 3] += v.w;
+        s0[r] = u.x + v.x; s0[r + 1] = u.y + v.y; s0[r + 2] = u.z + v.z; s0[r + 3] = u.w + v.w;
       }
-      const bool partial = j0 + kBN > w_lim_lo;
-      const int vlim = lim - j0 - 4 * g;  // key j0 + 4g + C visible <=> C < vlim
-      float mx = -INFINITY;
+      V8 vring[kPvDepth];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int C = 8 * (r >> 2) + (r & 3);
-        float x = s0[r] * scale2;
-        if (partial) x = (C < vlim) ? x : -INFINITY;
-        s0[r] = x;
-        mx = fmaxf(mx, x);
+      for (int c = 0; c < kPvDepth; ++c) vring[c] = load_v(c);
+      // Row max of the scaled scores; the exponent below is fma(s, kmul, -m):
+      // full tiles keep the raw scores (kmul = scale, max taken on the raw
+      // values, exact since scaling is monotonic), partial tiles store the
+      // scaled, masked scores (kmul = 1).
+      float mx = -INFINITY;
+      float kmul = scale2;
+      if (j0 + kBN > w_lim_lo) {
+        // Partial tile: key j0 + 4g + C is visible to this row iff C < vlim.
+        const int vlim = lim - j0 - 4 * (opaque_lane() >> 5);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int C = 8 * (r >> 2) + (r & 3);
+          const float x = (C < vlim) ? s0[r] * scale2 : -INFINITY;
+          s0[r] = x;
+          mx = fmaxf(mx, x);
+        }
+        kmul = 1.0f;
+      } else if (scale2 >= 0.0f) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+        mx *= scale2;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, -s0[r]);
+        mx *= -scale2;
       }
       mx = max_with_other_half(mx);
       // Lazy rescale: keep the reference max unless a row grew by > 2^8.  Both
@@ -290,7 +385,7 @@ __global__ void __launch_bounds__(512, 1)
       float psum = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = fast_exp2(s0[r] - m_use);
+        s0[r] = fast_exp2(__builtin_fmaf(s0[r], kmul, -m_use));
         psum += s0[r];
       }
       l_run += psum;
@@ -301,18 +396,10 @@ __global__ void __launch_bounds__(512, 1)
         p1[e] = (T)s0[8 + e];
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          // Keys 16kc + tr_row and the same + 8 (slot + 2), dims d .. d+3.
-          const int d = 32 * dt + tr_col;
-          const T* src0 = &lat[lat_slot(16 * kc + tr_row) * kLatRow + d];
-          const T* src1 = src0 + 2 * kLatRow;
-          const s16x4 lo = lds_read_tr16(src0);
-          const s16x4 hi = lds_read_tr16(src1);
-          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = mfma32(__builtin_bit_cast(V8, both), kc == 0 ? p0 : p1, o[dt]);
-        }
+      for (int i = 0; i < 2 * NDT; ++i) {
+        const V8 a = vring[i % kPvDepth];
+        if (i + kPvDepth < 2 * NDT) vring[i % kPvDepth] = load_v(i + kPvDepth);
+        o[i & 7] = mfma32(a, (i >> 3) == 0 ? p0 : p1, o[i & 7]);
       }
     }
   };
@@ -320,25 +407,28 @@ __global__ void __launch_bounds__(512, 1)
   // Writes the segment's result: the final output (and natural-log LSE) when the
   // segment covers the whole sequence, else the normalised partial output and
   // its log2-domain LSE.
-  auto seg_end = [&]() __attribute__((always_inline)) {
+  auto seg_end = [&](int seg) __attribute__((always_inline)) {
     if (!w_active) return;
     const float l_tot = sum_with_other_half(l_run);
     if (!row_ok) return;
-    const int4 sg = sload_int4(&segs[cs]);
+    const int4 sg = sload_int4(&segs[seg]);
     const int4 sq = sload_int4(&seqs[sg.x]);
     const int4 sq2 = sload_int4(&seqs2[sg.x]);
+    const int ln = opaque_lane();
+    const int mr = row_base + 32 * pr + (ln & 31);
+    const int gl = ln >> 5;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse2 = l_tot > 0.0f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     T* orow;
     if (sg.w < 0) {
-      orow = (T*)p.out + ((long long)sq.z * H + m) * kDv;
-      if (p.lse != nullptr && g == 0 && hf == 0) p.lse[(long long)sq.z * H + m] = lse2 * kLn2;
+      orow = (T*)p.out + ((long long)sq.z * H + mr) * kDv;
+      if (p.lse != nullptr && gl == 0 && hf == 0) p.lse[(long long)sq.z * H + mr] = lse2 * kLn2;
     } else {
-      const long long prow = (long long)sq2.x + (long long)sg.w * sq2.y + m;
+      const long long prow = (long long)sq2.x + (long long)sg.w * sq2.y + mr;
       orow = (T*)p.part_o + prow * kDv;
-      if (g == 0 && hf == 0) p.part_lse[prow] = lse2;
+      if (gl == 0 && hf == 0) p.part_lse[prow] = lse2;
     }
-    orow += 256 * hf + 4 * g;
+    orow += 256 * hf + 4 * gl;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -351,40 +441,76 @@ __global__ void __launch_bounds__(512, 1)
     }
   };
 
-  // ---- prologue: loads of the first two tiles ----
-  issue_tile(tile_block(), tbuf);
-  ld_advance();
-  if (n_total > 1) {
-    issue_tile(tile_block(), tbuf + kBufElems);
-    ld_advance();
-  }
-  int blk_next = (n_total > 2) ? tile_block() : 0;
-  end_of_tile(false);
-  bool first = true;  // the compute cursor sits on the first tile of a segment
+  // Moves the compute cursor past its current tile; true when that tile was the
+  // last of its segment.
+  auto advance_cursor = [&]() -> bool {
+    if (cj + kBN < ck1) {
+      cj += kBN;
+      return false;
+    }
+    cs = next_valid(cs + 1);
+    if (cs < s_end) {
+      const int4 sg = sload_int4(&segs[cs]);
+      cj = sg.y; ck1 = sg.z;
+    }
+    return true;
+  };
 
-  // ---- main loop: tile t computes from buffer t % 3 while tiles t+1 and t+2 load ----
+  // ---- prologue: loads of the first two tiles, queries of the first segment ----
+  const bool loader = w < 4;
+  int blk_next = 0;
+  if (loader) {
+    issue(tile_block(), tbuf);
+    ld_advance();
+    if (n_total > 1) {
+      issue(tile_block(), tbuf + kBufElems);
+      ld_advance();
+    }
+    if (n_total > 2) blk_next = tile_block();
+  }
+  load_q(cs);
+  reset_state(cs);
+  wait_tiles(false);
+  lds_barrier();
+
+  // ---- main loop ----
+  // Waves 0..3 (group A) and 4..7 (group B) share the SIMDs one to one.  Both
+  // run the same two-stage step per tile -- partial scores; barrier; loads of
+  // tile t+2 (group A), softmax and PV; barrier -- but B enters one barrier
+  // late, so B's partial scores of tile t overlap A's softmax and PV of tile t,
+  // and B's softmax and PV of tile t overlap A's partial scores of tile t+1:
+  // one wave's MFMA work runs beside the other's VALU work.  Only A loads
+  // tiles: its wait before the barrier that ends its step t publishes tile
+  // t+1 to both groups before either reads it, and the buffer it refills (that
+  // of tile t-1) was last read by B before the barrier that ends A's stage of
+  // tile t.  A group that finishes a segment writes its result and loads the
+  // next segment's queries inside its own step.
+  if (!loader) lds_barrier();
   for (int t = 0; t < n_total; ++t) {
-    if (first) seg_begin();
-    const int buf = t % 3;
-    if (t + 2 < n_total) {
-      issue_tile(blk_next, tbuf + ((t + 2) % 3) * kBufElems);
+    const T* cur = tbuf + (t % 3) * kBufElems;
+    qk_part(cur);
+    // Last tile of the segment: its queries are no longer needed; fetch the
+    // next segment's now.
+    if (cj + kBN >= ck1) {
+      const int nxt = next_valid(cs + 1);
+      if (nxt < s_end) load_q(nxt);
+    }
+    lds_barrier();  // exchange slots written; the direct loads in flight stay in flight
+    if (loader && t + 2 < n_total) {
+      issue(blk_next, tbuf + ((t + 2) % 3) * kBufElems);
       ld_advance();
       if (t + 3 < n_total) blk_next = tile_block();
     }
-    compute(tbuf + buf * kBufElems);
-    first = cj + kBN >= ck1;
-    if (first) {
-      seg_end();
-      cs = next_valid(cs + 1);
-      if (cs < s_end) {
-        const int4 sg = sload_int4(&segs[cs]);
-        cj = sg.y; ck1 = sg.z;
-      }
-    } else {
-      cj += kBN;
+    smpv_part(cur);
+    const int done = cs;
+    if (advance_cursor()) {
+      seg_end(done);
+      if (cs < s_end) reset_state(cs);
     }
-    end_of_tile(t + 2 < n_total);
+    if (loader) wait_tiles(t + 2 < n_total);
+    asm volatile("s_barrier" ::: "memory");
   }
+  if (loader) lds_barrier();
 }
 
 // Merge of a sequence's segment results: one wave per (token, head) row,

@@ -70,3 +70,11 @@ def test_traffic_summary_tracks_kernel_sources(tmp_path):
                      "traffic prefill_fwd_kernel<bf16,128,9> 4 10.0 20.0 40960\n")
     assert bench.read_traffic("prefill_fwd_kernel", str(stale)) is None
     assert bench.read_traffic("prefill_fwd_kernel", str(tmp_path / "missing.txt")) is None
+
+
+def test_short_kernel_names_bool_and_demangled():
+    assert bench.short_kernel_name(
+        "_ZN3mpa12_GLOBAL__N_116mla_split_kernelIDF16bLb1EEEvNS_9MlaParamsEPKi") == "mla_split_kernel<bf16,true>"
+    assert bench.short_kernel_name(
+        "void mpa::(anonymous namespace)::mla_split_kernel<bool _Accum, bool, E>(mpa::MlaParams)") == \
+        "mla_split_kernel<bf16,bool,E>"

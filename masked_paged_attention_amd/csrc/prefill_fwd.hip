@@ -335,9 +335,298 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   }
 }
 
+// headSize 128 with a power-of-two blockSize >= 64 (every 64-key tile inside one
+// cache block): the same computation, with K and V tiles brought into LDS by
+// direct global->LDS loads (no register staging).  LDS layout of a tile: 16
+// blocks of 4 rows (1 KB, one load instruction each) plus 16 bytes of padding;
+// inside a block the 16-byte chunks of row m are XOR-swizzled by 4m.  Both read
+// patterns -- 32 rows at one 16-byte column (QK operand) and 4 rows x 64 bytes
+// (V^T transpose read) -- then hit distinct bank groups, and each lane needs 4
+// base addresses per pattern (the rest are immediate offsets).
+template <typename T, int MASK>
+__global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
+                                                             const int32_t* __restrict__ block_tables) {
+  using V8 = typename Vec<T>::x8;
+  using V4 = typename Vec<T>::x4;
+  constexpr int D = 128;
+  constexpr bool kCausal = MASK != 0;
+  constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
+  constexpr bool kAlibiSqrt = MASK == 4;
+  constexpr int NC = D / 16;              // 16-wide contraction chunks of QK^T
+  constexpr int NDT = D / 32;             // 32-row tiles of O^T
+  constexpr int kRowBytes = D * (int)sizeof(T);   // 256
+  constexpr int kBlkBytes = 4 * kRowBytes + 16;   // 1040
+  constexpr int kTileBytes = 16 * kBlkBytes;      // 64 rows
+  constexpr int kBufBytes = 2 * kTileBytes;       // K tile, then V tile
+
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
+
+  const int4 item = p.items[blockIdx.x];
+  const int b = item.x;
+  if (b < 0) return;
+  const int head0 = item.y;
+  const int row0 = item.z;
+  const int4 sq = p.seqs[b];
+  const int L = sq.x;
+  const int kv = sq.y;
+  const long long qs = (long long)(unsigned)sq.z | ((long long)sq.w << 32);
+  const int prefix = kv - L;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int g = l >> 5;   // which half of the wave
+  const int lq = l & 31;  // query column of this lane
+  const int hpw = p.heads_per_item;
+  const int head = head0 + (w % hpw);
+  const int wrow0 = row0 + (w / hpw) * kRowsPerWave;
+  const int rows_per_item = kRowsPerWave * kWaves / hpw;
+  const int kvh = head0 / (p.head_num / p.kv_head_num);
+  const long long q_row_stride = (long long)p.head_num * D;
+  const unsigned kv_row_bytes = (unsigned)p.kv_head_num * (unsigned)kRowBytes;
+
+  const int item_rows_end = min(L, row0 + rows_per_item);
+  const int wg_keys = kCausal ? min(kv, prefix + item_rows_end) : kv;
+  const int n_tiles = (wg_keys + kBN - 1) / kBN;
+  const bool w_active = wrow0 < L;
+  const int w_rows_end = min(L, wrow0 + kRowsPerWave);
+  const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
+  const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+
+  // Q^T operand: lane l holds query row wrow0 + lq, dims 16c + 8g .. +8.
+  V8 qreg[NC];
+  {
+    const int qi = wrow0 + lq;
+    const T* qrow = (const T*)p.q + (qs + qi) * q_row_stride + (long long)head * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (qi < L) {
+        qreg[c] = *(const V8*)(qrow + 16 * c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
+      }
+    }
+  }
+
+  // ---- tile loads: wave w issues the 4-row blocks 4w .. 4w+3 of K and of V ----
+  // Lane l of a block load carries row 4i + l/16 (clamped to the last key),
+  // physical chunk l % 16 = logical chunk (l % 16) ^ 4(l / 16).
+  const int32_t* __restrict__ btab = block_tables + (long long)b * p.max_blocks;
+  const int lrow = l >> 4;
+  const unsigned lchunk16 = 16u * (unsigned)((l & 15) ^ (4 * lrow));
+  const unsigned lds_base = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds;
+  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf)
+      __attribute__((always_inline)) {
+    const unsigned off = (unsigned)min(4 * i + lrow, last) * kv_row_bytes + lchunk16;
+    dma16s_m0(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
+  };
+  struct TileSrc {
+    const char* k;
+    const char* v;
+    int last;
+  };
+  auto tile_src = [&](int t) -> TileSrc {
+    const int j0 = t * kBN;
+    const int blk = btab[j0 >> p.bs_shift];
+    const long long row = (long long)blk * p.block_size + (j0 & (p.block_size - 1));
+    const long long off = (row * p.kv_head_num + kvh) * D;
+    return {(const char*)((const T*)p.k + off), (const char*)((const T*)p.v + off), min(kBN, kv - j0) - 1};
+  };
+
+  // ---- LDS read addresses (bytes, without the buffer offset) ----
+  // QK operand of key row 32kb + lq, logical chunk q16 = 2c + g:
+  //   (8kb + lq/4) * 1040 + m * 256 + 16 * (q16 ^ 4m), m = lq % 4
+  //   = qa[(c / 2) ^ m] + 8320 kb + 32 (c % 2),  qa[x] = (lq/4) * 1040 + m * 256 + 64 x + 16 g.
+  const int mq = lq & 3;
+  unsigned qa[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    qa[x] = (unsigned)((lq >> 2) * kBlkBytes + mq * kRowBytes + 64 * (x ^ mq) + 16 * g);
+  // V^T operand, keys 16kc + 4g + s/4 (s = l % 16), dims 32dt + 16h + 4(s % 4):
+  //   (4kc + g) * 1040 + mv * 256 + 16 * ((4dt + 2h + (s%4)/2) ^ 4mv) + 8 (s % 2)
+  //   = va[dt] + 4160 kc;  the keys + 8 are 2 blocks (2080 bytes) further.
+  const int sl = l & 15;
+  const int mv = sl >> 2;
+  const int hh = (l >> 4) & 1;
+  unsigned va[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    va[dt] = (unsigned)(g * kBlkBytes + kTileBytes + mv * kRowBytes + 64 * (dt ^ mv) + 32 * hh +
+                        16 * ((sl & 3) >> 1) + 8 * (sl & 1));
+
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  const int a_lane = prefix + wrow0 + lq;
+  float slope2 = 0.0f;
+  if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
+  const float scale2 = p.scale2;
+
+  // prologue: tile 0
+  {
+    const TileSrc ts = tile_src(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      issue_block(0, 4 * w + i, ts.k, ts.last, 0);
+      issue_block(1, 4 * w + i, ts.v, ts.last, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  asm volatile("s_barrier" ::: "memory");
+
+  auto tile = [&](int t, auto BUF) __attribute__((always_inline)) {
+    constexpr int buf = decltype(BUF)::value;
+    constexpr unsigned kB = (unsigned)(buf * kBufBytes);
+    const int j0 = t * kBN;
+    const bool load_next = t + 1 < n_tiles;
+    TileSrc nx{};
+    if (load_next) nx = tile_src(t + 1);
+    // Loads of tile t+1 (into the other buffer), spread between the QK MFMAs.
+    auto issue_next = [&](int k) __attribute__((always_inline)) {
+      if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
+    };
+    if (w_active && j0 < w_keys) {
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // logical chunk c of key row 32kb + lq (qa maps it to its swizzled place)
+          const V8 a = *(const V8*)(lds + kB + qa[c >> 1] + 8320 * kb + 32 * (c & 1));
+          s[kb] = mfma32(a, qreg[c], s[kb]);
+          if (kb == 1) issue_next(c);
+        }
+      }
+      const int dbase = a_lane - j0 - 4 * g;
+      const int klim = kv - j0 - 4 * g;
+      const int vlim = kCausal ? min(klim, dbase + 1) : klim;
+      const bool partial = j0 + kBN > w_full_keys;
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float dbf = (float)dbase;
+      const float nbm = -slope2 * dbf - m_ref;
+      auto form_scores = [&](auto with_mask) __attribute__((always_inline)) -> float {
+        float m = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
+            float x;
+            if constexpr (kAlibiLinear) {
+              x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
+            } else if constexpr (kAlibiSqrt) {
+              x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
+            } else {
+              x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
+            }
+            if constexpr (decltype(with_mask)::value) x = (C < vlim) ? x : -INFINITY;
+            s[kb][r] = x;
+            m = fmaxf(m, x);
+          }
+        }
+        return m;
+      };
+      float mx;
+      if (partial) {
+        mx = form_scores(std::true_type{});
+      } else {
+        mx = form_scores(std::false_type{});
+      }
+      mx = max_with_other_half(mx);
+      const bool need = (m_run == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(m_run, m_ref + mx);
+        const float delta = (m_new == -INFINITY) ? 0.0f : m_new - m_ref;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(s[kb][r]);
+          s[kb][r] = e;
+          psum += e;
+        }
+      }
+      l_run += psum;
+      V8 pk[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[kc][e] = (T)s[kc >> 1][8 * (kc & 1) + e];
+      }
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const char* src = lds + kB + va[dt] + 4160 * kc;
+          const s16x4 lo = lds_read_tr16((const T*)src);
+          const s16x4 hi = lds_read_tr16((const T*)(src + 2080));
+          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = mfma32(__builtin_bit_cast(V8, both), pk[kc], o[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) issue_next(k);
+    }
+    // Tile t+1 has landed (each wave waits for its own loads; the barrier
+    // publishes them and ends every read of this buffer).
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!w_active) return;
+  const float l_tot = sum_with_other_half(l_run);
+  const int i = wrow0 + lq;
+  if (i >= L) return;
+  const float inv = 1.0f / l_tot;
+  T* orow = (T*)p.out + (qs + i) * q_row_stride + (long long)head * D + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      V4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * rg + e] * inv);
+      *(V4*)(orow + 32 * dt + 8 * rg) = v;
+    }
+  }
+  if (p.lse != nullptr && g == 0) {
+    float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if constexpr (MASK == 5) lse += p.slopes[head] * (float)a_lane;
+    p.lse[(qs + i) * p.head_num + head] = lse;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
+  if (D == 128 && p.bs_shift >= 6) {
+    switch (mask_type) {
+      case 0: hipLaunchKernelGGL((prefill_dma_kernel<T, 0>), g, blk, 0, s, p, p.block_tables); break;
+      case 3: hipLaunchKernelGGL((prefill_dma_kernel<T, 3>), g, blk, 0, s, p, p.block_tables); break;
+      case 4: hipLaunchKernelGGL((prefill_dma_kernel<T, 4>), g, blk, 0, s, p, p.block_tables); break;
+      case 5: hipLaunchKernelGGL((prefill_dma_kernel<T, 5>), g, blk, 0, s, p, p.block_tables); break;
+      case 9: hipLaunchKernelGGL((prefill_dma_kernel<T, 9>), g, blk, 0, s, p, p.block_tables); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (mask_type) {
     case 0: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 0>), g, blk, 0, s, p); break;
     case 3: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 3>), g, blk, 0, s, p); break;

@@ -97,6 +97,21 @@ __device__ __forceinline__ void dma16s_m0(const void* sbase, unsigned voffset, u
       : "memory");
 }
 
+// Same, without a memory clobber: the compiler may move ordinary memory
+// accesses across it.  For callers whose every ordering constraint on the
+// loaded LDS bytes runs through other volatile asm statements (waits and
+// barriers), which keep their order relative to this one.
+__device__ __forceinline__ void dma16s_m0_nomem(const void* sbase, unsigned voffset, unsigned m) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(sbase), "s"(m));
+}
+
 // Same, with the LDS destination given as a pointer.
 __device__ __forceinline__ void dma16s(const void* sbase, unsigned voffset, const void* lds_base) {
   dma16s_m0(sbase, voffset,

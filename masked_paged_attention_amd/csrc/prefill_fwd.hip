@@ -419,7 +419,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf)
       __attribute__((always_inline)) {
     const unsigned off = (unsigned)min(4 * i + lrow, last) * kv_row_bytes + lchunk16;
-    dma16s_m0(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
+    dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
   };
   struct TileSrc {
     const char* k;

@@ -98,7 +98,7 @@ KERNEL_FILES = ("masked_paged_attention_amd/csrc/prefill_fwd.hip",
                 "masked_paged_attention_amd/csrc/planner.cpp",
                 "masked_paged_attention_amd/csrc/api.cpp")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
-KERNEL_KEYS = ("prefill_fwd_kernel", "mla_split_kernel", "mla_combine_kernel")
+KERNEL_KEYS = ("prefill_dma_kernel", "prefill_fwd_kernel", "mla_split_kernel", "mla_combine_kernel")
 
 
 def kernel_source_digest():
@@ -421,10 +421,10 @@ def main():
             "decode_batch": int(m0.batch),
             "decode_kv_keys": int(np.sum(m0.context_lens)),
         },
-        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel<bf16,128,causal>",
+        "roofline": {"bound": "mfma", "kernel": "prefill_dma_kernel<bf16,causal>",
                      "achieved": round(p_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": read_traffic("prefill_fwd_kernel"),
+                     "traffic": read_traffic("prefill_dma_kernel"),
                      "per_launch_flops": int(p_flops), "ms": round(p_ms, 5)},
         "decode": {"value": round(m_gbs, 1), "unit": "GB/s", "frac_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
                    "ms": round(m_ms, 5), "bytes": int(m_bytes),

@@ -343,6 +343,16 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
 // patterns -- 32 rows at one 16-byte column (QK operand) and 4 rows x 64 bytes
 // (V^T transpose read) -- then hit distinct bank groups, and each lane needs 4
 // base addresses per pattern (the rest are immediate offsets).
+//
+// With an ALiBi mask the key tiles are visited from the last one down: the
+// largest biases sit next to the diagonal, so the running max is set by the
+// first tile and rarely moves, and a tile that every row sees needs no max at
+// all -- P = exp2(score - m_run) is formed at once, and a lane's partial row
+// sum above 2^8 (the only way some P can exceed 2^8) sends the tile through
+// the full path, which finds the tile max and moves the reference.  The result
+// is the same either way: only the reference of the exponent differs.  Other
+// masks visit the tiles in key order (the workgroups of one head then sweep
+// the cache together) and always take the full path.
 template <typename T, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
                                                              const int32_t* __restrict__ block_tables) {
@@ -352,12 +362,14 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   constexpr bool kCausal = MASK != 0;
   constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
   constexpr bool kAlibiSqrt = MASK == 4;
+  constexpr bool kReverse = kAlibiLinear || kAlibiSqrt;
   constexpr int NC = D / 16;              // 16-wide contraction chunks of QK^T
   constexpr int NDT = D / 32;             // 32-row tiles of O^T
   constexpr int kRowBytes = D * (int)sizeof(T);   // 256
   constexpr int kBlkBytes = 4 * kRowBytes + 16;   // 1040
   constexpr int kTileBytes = 16 * kBlkBytes;      // 64 rows
   constexpr int kBufBytes = 2 * kTileBytes;       // K tile, then V tile
+  constexpr float kSumLimit = 256.0f;             // 2^kRescaleSlack
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
 
@@ -391,6 +403,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const bool w_active = wrow0 < L;
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
   const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
+  const int w_tiles = w_active ? (w_keys + kBN - 1) / kBN : 0;  // tiles 0 .. w_tiles-1 matter here
   const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
 
   // Q^T operand: lane l holds query row wrow0 + lq, dims 16c + 8g .. +8.
@@ -411,27 +424,29 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 
   // ---- tile loads: wave w issues the 4-row blocks 4w .. 4w+3 of K and of V ----
   // Lane l of a block load carries row 4i + l/16 (clamped to the last key),
-  // physical chunk l % 16 = logical chunk (l % 16) ^ 4(l / 16).
+  // physical chunk l % 16 = logical chunk (l % 16) ^ 4(l / 16).  Iteration u
+  // handles tile tile_of(u).
   const int32_t* __restrict__ btab = block_tables + (long long)b * p.max_blocks;
   const int lrow = l >> 4;
   const unsigned lchunk16 = 16u * (unsigned)((l & 15) ^ (4 * lrow));
   const unsigned lds_base = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds;
-  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf)
-      __attribute__((always_inline)) {
-    const unsigned off = (unsigned)min(4 * i + lrow, last) * kv_row_bytes + lchunk16;
-    dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
-  };
+  auto tile_of = [&](int u) { return kReverse ? n_tiles - 1 - u : u; };
+  auto block_of = [&](int u) -> int { return (u < n_tiles) ? btab[(tile_of(u) * kBN) >> p.bs_shift] : 0; };
   struct TileSrc {
     const char* k;
     const char* v;
     int last;
   };
-  auto tile_src = [&](int t) -> TileSrc {
-    const int j0 = t * kBN;
-    const int blk = btab[j0 >> p.bs_shift];
+  auto tile_src = [&](int u, int blk) -> TileSrc {
+    const int j0 = tile_of(u) * kBN;
     const long long row = (long long)blk * p.block_size + (j0 & (p.block_size - 1));
     const long long off = (row * p.kv_head_num + kvh) * D;
     return {(const char*)((const T*)p.k + off), (const char*)((const T*)p.v + off), min(kBN, kv - j0) - 1};
+  };
+  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf)
+      __attribute__((always_inline)) {
+    const unsigned off = (unsigned)min(4 * i + lrow, last) * kv_row_bytes + lchunk16;
+    dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
   };
 
   // ---- LDS read addresses (bytes, without the buffer offset) ----
@@ -458,6 +473,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+  f32x16 s[2];
+  V8 pk[4];
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const int a_lane = prefix + wrow0 + lq;
@@ -465,9 +482,112 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
   const float scale2 = p.scale2;
 
-  // prologue: tile 0
+  // P of tile t from S^T (in s): running max and sum (see the comment above).
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * kBN;
+    const int dbase = a_lane - j0 - 4 * g;
+    const int klim = kv - j0 - 4 * g;
+    const int vlim = kCausal ? min(klim, dbase + 1) : klim;
+    const bool partial = j0 + kBN > w_full_keys;
+    const float dbf = (float)dbase;
+    float x[2][16];
+    float psum;
+    auto score = [&](int kb, int r, float m_ref, float nbm) __attribute__((always_inline)) -> float {
+      const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
+      if constexpr (kAlibiLinear) {
+        return __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
+      } else if constexpr (kAlibiSqrt) {
+        return __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
+      } else {
+        return __builtin_fmaf(s[kb][r], scale2, -m_ref);
+      }
+    };
+    bool done = false;
+    if (kReverse && !partial && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+      const float nbm = -slope2 * dbf - m_run;
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(score(kb, r, m_run, nbm));
+          x[kb][r] = e;
+          ps[r & 3] += e;
+        }
+      }
+      psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      done = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) == 0;
+    }
+    if (!done) {
+      // Full path: tile max; the reference moves when a row's max grows by
+      // more than 2^8 (or on the row's first visible key).
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      const float nbm = -slope2 * dbf - m_ref;
+      // scores and the lane max, with or without the per-element predicate
+      // (a wave-uniform branch between two straight-line versions)
+      auto form = [&](auto with_mask) __attribute__((always_inline)) -> float {
+        float m = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
+            float v = score(kb, r, m_ref, nbm);
+            if constexpr (decltype(with_mask)::value) v = (C < vlim) ? v : -INFINITY;
+            x[kb][r] = v;
+            m = fmaxf(m, v);
+          }
+        }
+        return m;
+      };
+      float m;
+      if (partial) {
+        m = form(std::true_type{});
+      } else {
+        m = form(std::false_type{});
+      }
+      const float mx = max_with_other_half(m);
+      const bool need = (m_run == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(m_run, m_ref + mx);
+        const float delta = (m_new == -INFINITY) ? 0.0f : m_new - m_ref;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] -= delta;
+        }
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
+      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(x[kb][r]);
+          x[kb][r] = e;
+          ps[r & 3] += e;
+        }
+      }
+      psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+    l_run += psum;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[kc][e] = (T)x[kc >> 1][8 * (kc & 1) + e];
+    }
+  };
+
+  // prologue: tile of iteration 0, then a full wait the compiler sees (Q has
+  // landed too, so no wait for Q is left for it to place inside the loop,
+  // where it would also drain the tile loads in flight).
+  int blk_next = block_of(1);  // block id of the next iteration's tile
   {
-    const TileSrc ts = tile_src(0);
+    const TileSrc ts = tile_src(0, block_of(0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       issue_block(0, 4 * w + i, ts.k, ts.last, 0);
@@ -477,94 +597,33 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   __builtin_amdgcn_s_waitcnt(0xF70);
   asm volatile("s_barrier" ::: "memory");
 
-  auto tile = [&](int t, auto BUF) __attribute__((always_inline)) {
+  auto iteration = [&](int u, auto BUF) __attribute__((always_inline)) {
     constexpr int buf = decltype(BUF)::value;
     constexpr unsigned kB = (unsigned)(buf * kBufBytes);
-    const int j0 = t * kBN;
-    const bool load_next = t + 1 < n_tiles;
+    const int t = tile_of(u);
+    const bool load_next = u + 1 < n_tiles;
     TileSrc nx{};
-    if (load_next) nx = tile_src(t + 1);
-    // Loads of tile t+1 (into the other buffer), spread between the QK MFMAs.
+    if (load_next) nx = tile_src(u + 1, blk_next);
+    // Loads of the next iteration's tile (into the other buffer), spread between
+    // the QK MFMAs.
     auto issue_next = [&](int k) __attribute__((always_inline)) {
       if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
     };
-    if (w_active && j0 < w_keys) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+    if (t < w_tiles) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          // logical chunk c of key row 32kb + lq (qa maps it to its swizzled place)
           const V8 a = *(const V8*)(lds + kB + qa[c >> 1] + 8320 * kb + 32 * (c & 1));
           s[kb] = mfma32(a, qreg[c], s[kb]);
           if (kb == 1) issue_next(c);
         }
       }
-      const int dbase = a_lane - j0 - 4 * g;
-      const int klim = kv - j0 - 4 * g;
-      const int vlim = kCausal ? min(klim, dbase + 1) : klim;
-      const bool partial = j0 + kBN > w_full_keys;
-      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
-      const float dbf = (float)dbase;
-      const float nbm = -slope2 * dbf - m_ref;
-      auto form_scores = [&](auto with_mask) __attribute__((always_inline)) -> float {
-        float m = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
-            float x;
-            if constexpr (kAlibiLinear) {
-              x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
-            } else if constexpr (kAlibiSqrt) {
-              x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
-            } else {
-              x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
-            }
-            if constexpr (decltype(with_mask)::value) x = (C < vlim) ? x : -INFINITY;
-            s[kb][r] = x;
-            m = fmaxf(m, x);
-          }
-        }
-        return m;
-      };
-      float mx;
-      if (partial) {
-        mx = form_scores(std::true_type{});
-      } else {
-        mx = form_scores(std::false_type{});
-      }
-      mx = max_with_other_half(mx);
-      const bool need = (m_run == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = fmaxf(m_run, m_ref + mx);
-        const float delta = (m_new == -INFINITY) ? 0.0f : m_new - m_ref;
-        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kb][r]);
-          s[kb][r] = e;
-          psum += e;
-        }
-      }
-      l_run += psum;
-      V8 pk[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pk[kc][e] = (T)s[kc >> 1][8 * (kc & 1) + e];
-      }
+      // block id two iterations ahead, read while the softmax runs
+      blk_next = block_of(u + 2);
+      softmax(t);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -579,15 +638,16 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
+      blk_next = block_of(u + 2);
     }
-    // Tile t+1 has landed (each wave waits for its own loads; the barrier
+    // The next tile has landed (each wave waits for its own loads; the barrier
     // publishes them and ends every read of this buffer).
     __builtin_amdgcn_s_waitcnt(0xF70);
     asm volatile("s_barrier" ::: "memory");
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) tile(t + 1, std::integral_constant<int, 1>{});
+  for (int u = 0; u < n_tiles; u += 2) {
+    iteration(u, std::integral_constant<int, 0>{});
+    if (u + 1 < n_tiles) iteration(u + 1, std::integral_constant<int, 1>{});
   }
 
   if (!w_active) return;

@@ -78,3 +78,10 @@ def test_short_kernel_names_bool_and_demangled():
     assert bench.short_kernel_name(
         "void mpa::(anonymous namespace)::mla_split_kernel<bool _Accum, bool, E>(mpa::MlaParams)") == \
         "mla_split_kernel<bf16,bool,E>"
+
+
+def test_short_kernel_name_of_the_dma_prefill_kernel():
+    import bench
+    assert bench.short_kernel_name(
+        "_ZN3mpa12_GLOBAL__N_118prefill_dma_kernelIDF16bLi9EEEvNS_13PrefillParamsEPKi") == \
+        "prefill_dma_kernel<bf16,9>"

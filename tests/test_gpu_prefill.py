@@ -143,3 +143,22 @@ def test_packed_equals_padded_full_size():
         L = int(c.seq_len[b])
         assert torch.equal(o1[s1[b]:s1[b] + L], o2[s2[b]:s2[b] + L])
         assert torch.equal(l1[s1[b]:s1[b] + L], l2[s2[b]:s2[b] + L])
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("mask", [3, 4, 5])
+def test_alibi_score_spikes_move_the_running_max(dtype, mask):
+    # Keys far from the diagonal with very large dot products: visiting tiles from
+    # the diagonal down, the running max is set early and these keys then exceed
+    # it by far more than 2^8, which must move the reference (the full path).
+    log(f"case score spikes dtype={dtype} mask={mask}")
+    c = W.make_prefill(71 + mask, np.array([700, 300]), np.array([700, 500]), 4, 4, 128, 128, dtype,
+                       mask, 1.0 / np.sqrt(128), slopes="alibi", poison=False, name=f"spike-{dtype}-m{mask}")
+    bs = c.block_size
+    for b, keys in [(0, [5, 130, 131, 400]), (1, [3, 260])]:
+        for j in keys:
+            blk = int(c.block_tables[b, j // bs])
+            c.key[blk, j % bs] *= 25
+    c = c.to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)

@@ -125,6 +125,8 @@ def short_kernel_name(mangled):
                 inner = rest[1:rest.find(">")] if ">" in rest else ""
                 for a in inner.split(","):
                     a = a.strip()
+                    if a in ("bool", "E"):  # pieces of a garbled non-type argument
+                        continue
                     # (rocprofv3 prints the mangled __bf16, DF16b, as "bool _Accum")
                     args.append("bf16" if "bf" in a.lower() or "_Accum" in a else
                                 "fp16" if "16" in a and "float" in a.lower() else a)

@@ -395,6 +395,23 @@ def main():
                                 "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                 "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
         op4.close()
+        # LSE merge of 8 partials shaped like the prefix-encoder output (HBM-bound;
+        # 8 x 43 MB of partials exceed the 256 MB Infinity Cache).
+        print("bench: extra lse_merge", file=sys.stderr, flush=True)
+        n_parts = 8
+        rows = pc.n_tokens * pc.head_num
+        g = torch.Generator(device=dev).manual_seed(5)
+        o_parts = torch.randn((n_parts, pc.n_tokens, pc.head_num, pc.head_size), generator=g,
+                              device=dev).to(torch.bfloat16)
+        l_parts = torch.randn((n_parts, pc.n_tokens, pc.head_num), generator=g, device=dev) * 4.0
+        mo = torch.empty_like(o_parts[0])
+        ml = torch.empty_like(l_parts[0])
+        ms = time_op(torch, lambda: mpa.lse_merge(o_parts, l_parts, out=mo, lse=ml), 20, 3)
+        by = (n_parts + 1) * rows * (pc.head_size * 2 + 4)
+        extra["lse_merge"] = {"ms": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "parts": n_parts, "rows": rows, "head_dim": pc.head_size}
+        del o_parts, l_parts, mo, ml
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -171,6 +171,32 @@ mpaStatus mpaMLAGetWorkspaceSize(
  * LSE-weighted merge into attenOut / lse. */
 mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void *stream);
 
+/*
+ * Merge of attention partials over disjoint key ranges by their log-sum-exp
+ * (page "MLA", parameter table: the lse output, which the RING calcType requires;
+ * the same merge the MLA call applies to its split-KV partials).  Each part is
+ * the (output, LSE) of one call of this library over one key range, e.g. the
+ * chunks of a long prefix, or one GPU's range of a ring.  For row r and part s:
+ *   LSE_r = ln sum_s exp(lseParts[s][r]),
+ *   out[r] = sum_s exp(lseParts[s][r] - LSE_r) * oParts[s][r].
+ * A part with LSE = -inf (no key in its range) weighs nothing; a row whose
+ * parts are all -inf gets out = 0 and LSE = -inf.  One launch on `stream`;
+ * nothing is allocated.
+ *   oParts    dev [nParts, rows, headDim] dtype, contiguous (parts stacked)
+ *   lseParts  dev [nParts, rows] fp32, natural log (as written by the lse
+ *             outputs of PrefixEncoder and MLA)
+ *   nParts    >= 1;  rows >= 0 ((token, head) pairs);  headDim a multiple of 8,
+ *             8 .. 4096
+ *   dtype     MPA_FP16 or MPA_BF16
+ *   out       dev [rows, headDim] dtype (output); may not overlap the parts
+ *   lse       dev [rows] fp32 natural-log LSE (output), or NULL
+ * With rows = 0 nothing is launched and the pointers may be NULL.
+ * Errors: MPA_ERROR_INVALID_ARG for NULL pointers or out-of-range sizes (checked
+ * before any HIP call), MPA_ERROR_HIP if the launch fails.
+ */
+mpaStatus mpaLseMerge(const void *oParts, const float *lseParts, int32_t nParts, int64_t rows,
+                      int32_t headDim, int dtype, void *out, float *lse, void *stream);
+
 /* Releases an operation (NULL is accepted).  Must not be called while an
  * execution of it may still be running on a stream. */
 mpaStatus mpaDestroyOperation(mpaOperation *op);

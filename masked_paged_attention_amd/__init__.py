@@ -261,6 +261,35 @@ def mla(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, *, qk_scale, 
         op.close()
 
 
+def lse_merge(o_parts, lse_parts, *, out=None, lse=None, return_lse=True, stream=None):
+    """Merge attention partials over disjoint key ranges by their LSE (mpaLseMerge).
+
+    o_parts [nParts, ..., headDim] float16/bfloat16 and lse_parts [nParts, ...] fp32
+    (natural log), e.g. torch.stack of the (out, lse) pairs of several calls over
+    disjoint key ranges.  Returns out [..., headDim] (and its LSE with return_lse)."""
+    _need(o_parts.dtype in _DTYPES, "o_parts must be float16 or bfloat16")
+    _need(lse_parts.dtype == torch.float32, "lse_parts must be float32")
+    _need(o_parts.is_cuda and lse_parts.device == o_parts.device, "o_parts and lse_parts on one GPU")
+    _need(o_parts.dim() >= 2 and tuple(lse_parts.shape) == tuple(o_parts.shape[:-1]),
+          "o_parts [nParts, ..., headDim] and lse_parts [nParts, ...]")
+    _need(o_parts.is_contiguous() and lse_parts.is_contiguous(), "parts must be contiguous")
+    n_parts, head_dim = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel() if n_parts else 0
+    if out is None:
+        out = torch.empty(o_parts.shape[1:], dtype=o_parts.dtype, device=o_parts.device)
+    _need(out.dtype == o_parts.dtype and tuple(out.shape) == tuple(o_parts.shape[1:]) and out.is_contiguous(),
+          "out must be a contiguous tensor shaped like one part")
+    if lse is None and return_lse:
+        lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == tuple(lse_parts.shape[1:]) and lse.is_contiguous(),
+              "lse must be a contiguous float32 tensor shaped like one LSE part")
+    st = LIB.mpaLseMerge(_ptr(o_parts), _ptr(lse_parts), n_parts, rows, head_dim, _DTYPES[o_parts.dtype],
+                         _ptr(out), _ptr(lse), _stream(o_parts.device, stream))
+    _check(st, "mpaLseMerge")
+    return (out, lse) if lse is not None else out
+
+
 def plan_prefill(seq_len, kv_seq_len, mask_type, head_num, kv_head_num, head_size=128):
     """Host-only view of the prefill launch plan: (items [n, 4] int32 {b, head0, row0,
     n_tiles}, rows_per_item, keys_per_tile, heads_per_item)."""

@@ -31,6 +31,9 @@ SIGNATURES = {
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, numBlocks, blockSize, maxBlockNum
         ctypes.c_int, c_vp, c_vp, c_u64p, c_opp]),   # dtype, attenOut, lse, workspaceSize, op
     "mpaMLA": (ctypes.c_int32, [c_vp, ctypes.c_uint64, c_vp, c_vp]),
+    "mpaLseMerge": (ctypes.c_int32, [
+        c_vp, c_vp, ctypes.c_int32, ctypes.c_int64,  # oParts, lseParts, nParts, rows
+        ctypes.c_int32, ctypes.c_int, c_vp, c_vp, c_vp]),  # headDim, dtype, out, lse, stream
     "mpaDestroyOperation": (ctypes.c_int32, [c_vp]),
     "mpaGetErrorString": (ctypes.c_char_p, [ctypes.c_int32]),
     "mpaGetLastErrorMessage": (ctypes.c_char_p, []),

@@ -393,6 +393,33 @@ mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void
   return MPA_OK;
 }
 
+mpaStatus mpaLseMerge(const void* oParts, const float* lseParts, int32_t nParts, int64_t rows,
+                      int32_t headDim, int dtype, void* out, float* lse, void* stream) {
+  g_last_error.clear();
+  if (nParts < 1) return fail(MPA_ERROR_INVALID_ARG, "nParts must be >= 1 (got %d)", nParts);
+  if (rows < 0) return fail(MPA_ERROR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (rows > 0 && (!oParts || !lseParts || !out))
+    return fail(MPA_ERROR_INVALID_ARG, "oParts, lseParts and out are required");
+  if (headDim < 8 || headDim > 4096 || headDim % 8)
+    return fail(MPA_ERROR_INVALID_ARG, "headDim must be a multiple of 8 in [8, 4096] (got %d)", headDim);
+  if (dtype != MPA_FP16 && dtype != MPA_BF16) return fail(MPA_ERROR_INVALID_ARG, "dtype must be fp16 or bf16");
+  if (rows > ((int64_t)1 << 40) / headDim) return fail(MPA_ERROR_INVALID_ARG, "rows * headDim too large");
+  const uintptr_t mis = (uintptr_t)oParts | (uintptr_t)out;
+  if (mis & 15) return fail(MPA_ERROR_INVALID_ARG, "oParts and out must be 16-byte aligned");
+  mpa::LseMergeParams p;
+  p.o_parts = oParts;
+  p.lse_parts = lseParts;
+  p.out = out;
+  p.lse_out = lse;
+  p.rows = rows;
+  p.n_parts = nParts;
+  p.head_dim = headDim;
+  if (rows == 0) return MPA_OK;
+  hipError_t e = mpa::launch_lse_merge(p, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "LSE merge launch");
+  return MPA_OK;
+}
+
 mpaStatus mpaPrefixEncoderPlanInspect(const int32_t* seqLen, const int32_t* kvSeqLen, int32_t batch,
                                       int maskType, int32_t headNum, int32_t kvHeadNum,
                                       int32_t headSize, int32_t* items, int64_t capacity,

@@ -61,4 +61,16 @@ struct MlaParams {
 
 hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream);
 
+struct LseMergeParams {
+  const void* o_parts;         // [n_parts, rows, head_dim] partial outputs
+  const float* lse_parts;      // [n_parts, rows] natural-log LSE of each part
+  void* out;                   // [rows, head_dim]
+  float* lse_out;              // [rows] or null
+  long long rows;
+  int n_parts;
+  int head_dim;                // multiple of 8
+};
+
+hipError_t launch_lse_merge(const LseMergeParams& p, int dtype, hipStream_t stream);
+
 }  // namespace mpa

@@ -270,3 +270,23 @@ def test_mla_plan_small_problem_uses_few_pieces():
     pieces = sorted(set(int(x[4]) for x in segs))
     assert len(pieces) == 3            # 9 tiles, at least 4 tiles per piece
     assert all(x[1] % 32 == 0 for x in segs)
+
+
+def _merge(lib, o=16, l=32, n=2, rows=10, d=128, dtype=1, out=48, lse=64):
+    return lib.mpaLseMerge(ctypes.c_void_p(o), ctypes.c_void_p(l), n, rows, d, dtype,
+                           ctypes.c_void_p(out), ctypes.c_void_p(lse), ctypes.c_void_p(0))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(o=0), dict(l=0), dict(out=0), dict(n=0), dict(rows=-1), dict(d=12), dict(d=0),
+    dict(d=8192), dict(dtype=2), dict(o=24), dict(out=40),
+])
+def test_lse_merge_validation(lib, kw):
+    # every case is rejected on the host, before any HIP call
+    assert _merge(lib, **kw) == 1, lib.mpaGetLastErrorMessage()
+    assert lib.mpaGetLastErrorMessage()
+
+
+def test_lse_merge_zero_rows_is_a_no_op(lib):
+    assert _merge(lib, rows=0) == 0, lib.mpaGetLastErrorMessage()
+    assert _merge(lib, rows=0, o=0, l=0, out=0, lse=0) == 0, lib.mpaGetLastErrorMessage()

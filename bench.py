@@ -395,6 +395,21 @@ def main():
                                 "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                 "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
         op4.close()
+        # MLA calcType PREFILL: 4 prompts of 256 new tokens over 1-4k keys, causal.
+        print("bench: extra mla_prefill", file=sys.stderr, flush=True)
+        ctx_p = np.array([1024, 2048, 3072, 4096], dtype=np.int32)
+        ql_p = np.full(4, 256, dtype=np.int32)
+        mp = W.make_mla(81, ctx_p, ql_p, 128, 128, "bf16", 1, 3, 1, 1.0 / np.sqrt(192.0)).to(dev)
+        opp = mpa.MLA(mp.q_nope, mp.q_rope, mp.ct_kv, mp.k_rope, mp.block_tables, mp.context_lens,
+                      qk_scale=mp.qk_scale, q_seq_len=mp.q_seq_len, mask_type=mp.mask_type,
+                      calc_type=mp.calc_type, return_lse=True)
+        ms = time_op(torch, opp.run, 10, 3)
+        fl = mla_flops(mp.context_lens, mp.q_seq_len, mp.head_num, True)
+        extra["mla_prefill"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                                "shape": "4 x 256 tokens, ctx 1024..4096, 128 heads, causal"}
+        opp.close()
+        del mp, opp
         # LSE merge of 8 partials shaped like the prefix-encoder output (HBM-bound;
         # 8 x 43 MB of partials exceed the 256 MB Infinity Cache).
         print("bench: extra lse_merge", file=sys.stderr, flush=True)

@@ -129,6 +129,7 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
 #define MPA_MLA_MASK_SPEC 1        /* token t of q_len sees keys j <= contextLens - q_len + t */
 #define MPA_MLA_CALC_UNDEFINED 0   /* one query token per sequence */
 #define MPA_MLA_CALC_SPEC 1        /* qSeqLen tokens per sequence (speculative decode) */
+#define MPA_MLA_CALC_PREFILL 3     /* qSeqLen tokens per sequence (a whole new prompt); same masks */
 #define MPA_MLA_CACHE_KVCACHE 0    /* one concatenated cache ctKV [NB, BS, 1, 576], kRope NULL */
 #define MPA_MLA_CACHE_KROPE_CTKV 1 /* separate ctKV [NB, BS, 1, 512] and kRope [NB, BS, 1, 64] */
 
@@ -149,10 +150,12 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
  *   contextLens HOST [batch] int32 >= 1 (keys of each sequence, speculative
  *               tokens included)
  *   qSeqLen    HOST [batch] int32 in [1, contextLens[b]]; required iff calcType
- *              is MPA_MLA_CALC_SPEC, else NULL (one token per sequence)
+ *              is MPA_MLA_CALC_SPEC or MPA_MLA_CALC_PREFILL, else NULL (one token
+ *              per sequence)
  *   headNum    query heads (1..128 per token; > 0); kvHeadNum must be 1
  *   qkScale, maskType, calcType, cacheMode  see above (the int8 / NZ cache modes
- *              2 and 3 and calcType RING / PREFILL return MPA_ERROR_UNSUPPORTED)
+ *              2 and 3 and calcType RING return MPA_ERROR_UNSUPPORTED; RING's
+ *              single-GPU part is mpaLseMerge)
  *   batch, numBlocks, blockSize, maxBlockNum, dtype   as for PrefixEncoder
  *   attenOut   dev [T, headNum, 512] dtype (output)
  *   lse        dev [T, headNum] fp32 natural-log LSE (output), or NULL

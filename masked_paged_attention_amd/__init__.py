@@ -31,6 +31,7 @@ MLA_MASK_UNDEFINED = 0
 MLA_MASK_SPEC = 1
 MLA_CALC_UNDEFINED = 0
 MLA_CALC_SPEC = 1
+MLA_CALC_PREFILL = 3
 MLA_CACHE_KVCACHE = 0
 MLA_CACHE_KROPE_CTKV = 1
 

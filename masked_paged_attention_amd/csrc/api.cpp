@@ -286,14 +286,15 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
     return fail(MPA_ERROR_INVALID_ARG, "cacheMode 1 needs kRope");
   if (cacheMode == MPA_MLA_CACHE_KVCACHE && kRope)
     return fail(MPA_ERROR_INVALID_ARG, "cacheMode 0 keeps the rope part inside ctKV: kRope must be NULL");
-  if (calcType != MPA_MLA_CALC_UNDEFINED && calcType != MPA_MLA_CALC_SPEC)
-    return fail(MPA_ERROR_UNSUPPORTED, "calcType %d is not supported (0, 1)", calcType);
+  if (calcType != MPA_MLA_CALC_UNDEFINED && calcType != MPA_MLA_CALC_SPEC && calcType != MPA_MLA_CALC_PREFILL)
+    return fail(MPA_ERROR_UNSUPPORTED, "calcType %d is not supported (0, 1, 3)", calcType);
+  const bool many_tokens = calcType == MPA_MLA_CALC_SPEC || calcType == MPA_MLA_CALC_PREFILL;
   if (maskType != MPA_MLA_MASK_UNDEFINED && maskType != MPA_MLA_MASK_SPEC)
     return fail(MPA_ERROR_UNSUPPORTED, "maskType %d is not supported (0, 1)", maskType);
-  if (calcType == MPA_MLA_CALC_SPEC && !qSeqLen)
-    return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
-  if (calcType == MPA_MLA_CALC_UNDEFINED && qSeqLen)
-    return fail(MPA_ERROR_INVALID_ARG, "qSeqLen must be NULL unless calcType is SPEC");
+  if (many_tokens && !qSeqLen)
+    return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC / PREFILL needs qSeqLen");
+  if (!many_tokens && qSeqLen)
+    return fail(MPA_ERROR_INVALID_ARG, "qSeqLen must be NULL unless calcType is SPEC or PREFILL");
   if (!(qkScale == qkScale) || qkScale == INFINITY || qkScale == -INFINITY)
     return fail(MPA_ERROR_INVALID_ARG, "qkScale must be finite");
   if (numBlocks < 1 || blockSize < 1 || maxBlockNum < 1)
@@ -447,8 +448,8 @@ mpaStatus mpaMLAPlanInspect(const int32_t* contextLens, const int32_t* qSeqLen, 
   g_last_error.clear();
   if (!contextLens || batch < 1 || headNum <= 0) return fail(MPA_ERROR_INVALID_ARG, "invalid arguments");
   std::vector<int32_t> qlen(batch, 1);
-  if (calcType == MPA_MLA_CALC_SPEC) {
-    if (!qSeqLen) return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC needs qSeqLen");
+  if (calcType == MPA_MLA_CALC_SPEC || calcType == MPA_MLA_CALC_PREFILL) {
+    if (!qSeqLen) return fail(MPA_ERROR_INVALID_ARG, "calcType SPEC / PREFILL needs qSeqLen");
     for (int b = 0; b < batch; ++b) qlen[b] = qSeqLen[b];
   }
   mpa::MlaPlan plan = mpa::plan_mla(contextLens, qlen.data(), batch, headNum, 256);

@@ -7,8 +7,8 @@
 // are all -inf gets out = 0 and LSE = -inf.
 //
 // Streaming, HBM-bound: one thread per 16-byte chunk (8 elements) of one row;
-// the threads of a row read the same S LSE values (cached), weight them in
-// fp32 relative to the row max, and accumulate their chunk of every part.
+// the threads of a row read the same LSE values (cached) and accumulate their
+// chunk of every part in fp32, weighted relative to a running max.
 
 #include "device.h"
 #include "kernels.h"
@@ -23,27 +23,45 @@ constexpr float kLn2 = 0.6931471805599453f;
 template <typename T>
 __global__ void __launch_bounds__(256) lse_merge_kernel(LseMergeParams p) {
   using V8 = typename Vec<T>::x8;
+  constexpr int kGroup = 8;  // parts whose LSEs and chunks are loaded together
   const long long chunks_per_row = p.head_dim / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.rows * chunks_per_row) return;
   const long long r = idx / chunks_per_row;
   const int c = (int)(idx - r * chunks_per_row);
   const float* lse = p.lse_parts + r;
-  float mx = -INFINITY;
-  for (int s = 0; s < p.n_parts; ++s) mx = fmaxf(mx, lse[(long long)s * p.rows]);
+  const T* o = (const T*)p.o_parts + r * p.head_dim + 8 * c;
+  const long long part_stride = p.rows * p.head_dim;
+  // One pass, a group of parts at a time (one memory round trip per group): the
+  // running sum and accumulator are kept relative to the running max m.
+  float m = -INFINITY;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float tot = 0.0f;
-  if (mx != -INFINITY) {
-    const T* o = (const T*)p.o_parts + r * p.head_dim + 8 * c;
-    const long long part_stride = p.rows * p.head_dim;
-#pragma unroll 4
-    for (int s = 0; s < p.n_parts; ++s) {
-      const float w = __builtin_amdgcn_exp2f((lse[(long long)s * p.rows] - mx) * kLog2e);
-      const V8 v = *(const V8*)(o + s * part_stride);
+  for (int s0 = 0; s0 < p.n_parts; s0 += kGroup) {
+    V8 v[kGroup];
+    float lk[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const bool ok = s0 + k < p.n_parts;
+      v[k] = ok ? *(const V8*)(o + (long long)(s0 + k) * part_stride) : V8{};
+      lk[k] = ok ? lse[(long long)(s0 + k) * p.rows] : -INFINITY;
+    }
+    float gm = m;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) gm = fmaxf(gm, lk[k]);
+    if (gm == -INFINITY) continue;  // nothing seen so far
+    const float sc = __builtin_amdgcn_exp2f((m - gm) * kLog2e);  // 0 when m = -inf
+    tot *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const float w = __builtin_amdgcn_exp2f((lk[k] - gm) * kLog2e);  // 0 for -inf parts
       tot += w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)v[e], acc[e]);
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)v[k][e], acc[e]);
     }
+    m = gm;
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   V8 out;
@@ -51,7 +69,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(LseMergeParams p) {
   for (int e = 0; e < 8; ++e) out[e] = (T)(acc[e] * inv);
   *(V8*)((T*)p.out + r * p.head_dim + 8 * c) = out;
   if (c == 0 && p.lse_out != nullptr)
-    p.lse_out[r] = tot > 0.0f ? mx + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
+    p.lse_out[r] = tot > 0.0f ? m + __builtin_amdgcn_logf(tot) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -34,6 +34,7 @@ from .attention import (  # noqa: F401
     MLA_MASK_SPEC,
     MLA_CALC_UNDEFINED,
     MLA_CALC_SPEC,
+    MLA_CALC_PREFILL,
     prefix_encoder,
     prefix_encoder_rows,
     mla,

@@ -43,6 +43,7 @@ MLA_MASK_UNDEFINED = 0
 MLA_MASK_SPEC = 1
 MLA_CALC_UNDEFINED = 0
 MLA_CALC_SPEC = 1
+MLA_CALC_PREFILL = 3  # listing order on the MLA page: UNDEFINED, SPEC, RING, PREFILL
 
 ROW_CHUNK = 1024
 
@@ -207,9 +208,11 @@ def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, slopes,
 def _mla_qlens(batch, q_seq_len, calc_type):
     if calc_type == MLA_CALC_UNDEFINED:
         return [1] * batch
-    if calc_type == MLA_CALC_SPEC:
+    if calc_type in (MLA_CALC_SPEC, MLA_CALC_PREFILL):
+        # SPEC: a few speculative tokens; PREFILL ("prefill全量"): all new tokens of
+        # a prompt.  Both take qseqlen tokens per sequence with the same masks.
         if q_seq_len is None:
-            raise ValueError("calcType SPEC needs qseqlen")
+            raise ValueError("calcType SPEC / PREFILL needs qseqlen")
         return [int(x) for x in q_seq_len]
     raise ValueError(f"unsupported calcType {calc_type}")
 

@@ -153,10 +153,12 @@ def _mla(lib, **kw):
     (dict(cache=2), 2),
     (dict(cache=3), 2),
     (dict(calc=2), 2),                   # RING
-    (dict(calc=3), 2),                   # PREFILL
+    (dict(calc=3), 1),                   # PREFILL without qSeqLen
+    (dict(calc=4), 2),
     (dict(mask=2), 2),                   # MASK_FREE
     (dict(calc=1), 1),                   # SPEC without qSeqLen
-    (dict(ql=[1, 1]), 1),                # qSeqLen without SPEC
+    (dict(ql=[1, 1]), 1),                # qSeqLen without SPEC / PREFILL
+    (dict(calc=3, ql=[101, 2]), 1),      # PREFILL: more tokens than keys
     (dict(calc=1, ql=[0, 2]), 1),
     (dict(calc=1, ql=[101, 2]), 1),      # more tokens than keys
     (dict(kr=None), 1),                  # cacheMode 1 needs kRope

@@ -83,3 +83,26 @@ def test_mixed_lengths_cross_pieces(dtype):
     rows = sorted({(int(rng.integers(len(ctx))), int(rng.integers(128))) for _ in range(200)} |
                   {(b, h) for b in range(len(ctx)) for h in (0, 127)})
     check_mla(c, out, lse, rows=rows)
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_prefill_calc_type(mask):
+    # calcType PREFILL: whole prompts of new tokens (qSeqLen up to contextLens), with
+    # the same masks as SPEC; full parity on every (token, head).
+    log(f"case mla prefill q_len [40, 64, 9] H 16 mask={mask}")
+    c = W.make_mla(69, [40, 700, 300], [40, 64, 9], 16, 128, "bf16", mask, 3, 1, 1 / np.sqrt(192),
+                   poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse)
+
+
+def test_prefill_128_heads_sampled():
+    log("case mla prefill q_len [256, 130] H 128 causal (sampled rows)")
+    c = W.make_mla(71, [2048, 900], [256, 130], 128, 128, "bf16", 1, 3, 1, 1 / np.sqrt(192),
+                   poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(4)
+    T, H = c.n_tokens, c.head_num
+    rows = sorted({(int(rng.integers(T)), int(rng.integers(H))) for _ in range(160)} |
+                  {(0, 0), (T - 1, H - 1), (255, 5), (256, 7)})
+    check_mla(c, out, lse, rows=rows)

@@ -498,3 +498,32 @@ def test_compressed_tile_shapes_match_page():
     assert (M.MASK_ALIBI, M.MASK_ALIBI_SQRT, M.MASK_ALIBI_LEFT, M.MASK_CAUSAL) == (
         mt["MASK_TYPE_ALIBI_COMPRESS"], mt["MASK_TYPE_ALIBI_COMPRESS_SQRT"],
         mt["MASK_TYPE_ALIBI_COMPRESS_LEFT_ALIGN"], mt["MASK_TYPE_CAUSAL_MASK"])
+
+
+def test_mla_prefill_is_causal_self_attention():
+    # calcType PREFILL (MLA page, calcType row: "prefill全量") with the SPEC mask and
+    # whole prompts (qseqlen = contextLens) is causal self-attention over the prompt:
+    # the prefix-encoder rule with no prefix, and a brute-force row.
+    rng = np.random.default_rng(41)
+    B, H, bs = 2, 3, 8
+    ctx = np.array([13, 6])
+    need = [-(-int(c) // bs) for c in ctx]
+    nb = sum(need) + 1
+    bt = np.full((B, max(need)), nb - 1, dtype=np.int32)
+    bt[0, :need[0]] = [0, 1]
+    bt[1, :need[1]] = [2]
+    T = int(ctx.sum())
+    q_nope = rng.standard_normal((T, H, 512))
+    q_rope = rng.standard_normal((T, H, 64))
+    lat = rng.standard_normal((nb, bs, 1, 512))
+    rope = rng.standard_normal((nb, bs, 1, 64))
+    full = np.concatenate([lat, rope], axis=3)
+    o, l = oracle.mla(q_nope, q_rope, lat, rope, bt, ctx, ctx, H, 0.05, oracle.MLA_MASK_SPEC,
+                      oracle.MLA_CALC_PREFILL)
+    q = np.concatenate([q_nope, q_rope], axis=2)
+    og, lg = oracle.prefix_encoder(q, full, lat, bt, ctx, ctx, None, M.MASK_CAUSAL, H, 1, 0.05)
+    np.testing.assert_allclose(o, og, atol=1e-13)
+    np.testing.assert_allclose(l, lg, atol=1e-13)
+    # the first token of a prompt sees only key 0: its output is that key's latent row
+    np.testing.assert_allclose(o[0, 1], lat[bt[0, 0], 0, 0], atol=1e-12)
+    np.testing.assert_allclose(o[13, 2], lat[bt[1, 0], 0, 0], atol=1e-12)

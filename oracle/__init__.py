@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     MASK_ALIBI_SQRT,
     MASK_ALIBI_LEFT,
     MASK_CAUSAL,
+    MASK_CHUNKED_CAUSAL,
     MLA_MASK_UNDEFINED,
     MLA_MASK_SPEC,
     MLA_CALC_UNDEFINED,

@@ -38,6 +38,7 @@ MASK_ALIBI = _m.MASK_ALIBI
 MASK_ALIBI_SQRT = _m.MASK_ALIBI_SQRT
 MASK_ALIBI_LEFT = _m.MASK_ALIBI_LEFT
 MASK_CAUSAL = _m.MASK_CAUSAL
+MASK_CHUNKED_CAUSAL = _m.MASK_CHUNKED_CAUSAL
 
 MLA_MASK_UNDEFINED = 0
 MLA_MASK_SPEC = 1
@@ -128,7 +129,7 @@ def _check_prefix_args(seq_len, kv_seq_len, head_num, kv_head_num, mask_type, sl
 
 def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
                         slopes, mask_type, head_num, kv_head_num, qk_scale,
-                        rows, q_start_loc=None):
+                        rows, q_start_loc=None, chunk=None):
     """Oracle output for selected (b, i, h) triples only.
 
     ``rows`` is an iterable of (b, i, h) with 0 <= i < seq_len[b].  Returns
@@ -162,7 +163,7 @@ def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
             sel = ii[c0:c0 + ROW_CHUNK]
             a = (kv - L) + sel[:, None]
             j = np.arange(kv)[None, :]
-            vis = _m.visible(mask_type, a, j, kv)
+            vis = _m.visible(mask_type, a, j, kv, chunk)
             msk = np.where(vis, _m.bias(mask_type, slope, a, j), -np.inf)
             q = np.asarray(query[starts[b] + sel, h, :], dtype=np.float64)
             o, ls = attend(q, k_all, v_all, scale, msk)
@@ -173,7 +174,7 @@ def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
 
 def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, slopes,
                    mask_type, head_num, kv_head_num, qk_scale, q_start_loc=None,
-                   heads=None):
+                   heads=None, chunk=None):
     """Full oracle of the PrefixEncoder operation.
 
     Returns (O [nTokens, headNum, D] fp64, LSE [nTokens, headNum] fp64).  Rows that
@@ -195,7 +196,7 @@ def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, slopes,
             rows = [(b, i, h) for i in range(L)]
             o, ls = prefix_encoder_rows(query, key, value, block_tables, seq_len,
                                         kv_seq_len, slopes, mask_type, head_num,
-                                        kv_head_num, qk_scale, rows, q_start_loc)
+                                        kv_head_num, qk_scale, rows, q_start_loc, chunk)
             out[starts[b]:starts[b] + L, h] = o
             lse[starts[b]:starts[b] + L, h] = ls
     return out, lse

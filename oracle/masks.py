@@ -38,6 +38,12 @@ the design doc's ambiguity register):
 * causal (maskType 9, generated inside the operator) and the compressed norm mask
   used for RoPE models: j <= a_i;
 * maskType 0 (ours): no causal rule, keys limited only by kv_len (padding mask);
+* chunked local causal mask (ours, number 10): the LLaMA 4 chunked attention of
+  the page "终极指南：LLaMA模型的Transformer注意力掩码与填充处理技术解析", section
+  "本地注意力掩码生成" (the function body is elided there; the plainest reading
+  of a per-token chunk restriction combined with causality): with chunk size C,
+  a query at absolute position a sees the keys j <= a of its own chunk,
+  floor(j / C) == floor(a / C);
 * every type also hides keys j >= kv_len (padding / varlen boundary, nalar.dev
   article, sections "Causal mask dan padding mask menangani batas yang berbeda" and
   "Packing mengeluarkan padding dari representasi").
@@ -50,8 +56,9 @@ MASK_ALIBI = 3
 MASK_ALIBI_SQRT = 4
 MASK_ALIBI_LEFT = 5
 MASK_CAUSAL = 9
+MASK_CHUNKED_CAUSAL = 10
 
-CAUSAL_TYPES = (MASK_ALIBI, MASK_ALIBI_SQRT, MASK_ALIBI_LEFT, MASK_CAUSAL)
+CAUSAL_TYPES = (MASK_ALIBI, MASK_ALIBI_SQRT, MASK_ALIBI_LEFT, MASK_CAUSAL, MASK_CHUNKED_CAUSAL)
 ALIBI_TYPES = (MASK_ALIBI, MASK_ALIBI_SQRT, MASK_ALIBI_LEFT)
 
 # Edge of the compressed tiles (the [128,128] norm mask and the [256,256] ALiBi
@@ -59,10 +66,11 @@ ALIBI_TYPES = (MASK_ALIBI, MASK_ALIBI_SQRT, MASK_ALIBI_LEFT)
 TILE = 128
 
 
-def visible(mask_type, a, j, kv_len):
+def visible(mask_type, a, j, kv_len, chunk=None):
     """Boolean visibility of key position ``j`` for a query at absolute ``a``.
 
     ``a`` and ``j`` broadcast against each other (e.g. a[:, None], j[None, :]).
+    ``chunk`` is the chunk size of MASK_CHUNKED_CAUSAL (required for it only).
     """
     a = np.asarray(a)
     j = np.asarray(j)
@@ -71,6 +79,12 @@ def visible(mask_type, a, j, kv_len):
         vis = vis & (j <= a)
     elif mask_type != MASK_NONE:
         raise ValueError(f"unknown mask type {mask_type}")
+    if mask_type == MASK_CHUNKED_CAUSAL:
+        if chunk is None or int(chunk) < 1:
+            raise ValueError("the chunked mask needs a chunk size >= 1")
+        vis = vis & (j // int(chunk) == a // int(chunk))
+    elif chunk is not None:
+        raise ValueError("a chunk size goes with the chunked mask only")
     return vis
 
 
@@ -79,7 +93,7 @@ def bias(mask_type, slope, a, j):
     a = np.asarray(a, dtype=np.float64)
     j = np.asarray(j, dtype=np.float64)
     slope = float(slope)
-    if mask_type in (MASK_NONE, MASK_CAUSAL):
+    if mask_type in (MASK_NONE, MASK_CAUSAL, MASK_CHUNKED_CAUSAL):
         return np.zeros(np.broadcast(a, j).shape)
     if mask_type == MASK_ALIBI:
         return slope * (j - a)

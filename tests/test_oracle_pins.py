@@ -527,3 +527,72 @@ def test_mla_prefill_is_causal_self_attention():
     # the first token of a prompt sees only key 0: its output is that key's latent row
     np.testing.assert_allclose(o[0, 1], lat[bt[0, 0], 0, 0], atol=1e-12)
     np.testing.assert_allclose(o[13, 2], lat[bt[1, 0], 0, 0], atol=1e-12)
+
+
+def _brute_chunked(query, key, value, bt, seq_len, kv_seq_len, H, KVH, scale, chunk):
+    """Pure-Python chunked-local causal attention: row at absolute a sees keys j <= a
+    with j // chunk == a // chunk (one key at a time through the block table)."""
+    bs = key.shape[1]
+    g = H // KVH
+    scale = float(np.float32(scale))
+    res, row0 = {}, 0
+    for b in range(len(seq_len)):
+        L, kv = int(seq_len[b]), int(kv_seq_len[b])
+        for h in range(H):
+            for i in range(L):
+                a = kv - L + i
+                q = query[row0 + i][h]
+                sc, vals = [], []
+                for j in range((a // chunk) * chunk, a + 1):
+                    blk = int(bt[b][j // bs])
+                    k = key[blk][j % bs][h // g]
+                    sc.append(scale * math.fsum(float(x) * float(y) for x, y in zip(q, k)))
+                    vals.append(value[blk][j % bs][h // g])
+                m = max(sc)
+                w = [math.exp(s - m) for s in sc]
+                tot = math.fsum(w)
+                o = np.array([math.fsum(w[n] * float(vals[n][d]) for n in range(len(w))) / tot
+                              for d in range(len(vals[0]))])
+                res[(row0 + i, h)] = (o, m + math.log(tot))
+        row0 += L
+    return res
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 8, 64])
+def test_chunked_mask_brute_force(chunk):
+    rng = np.random.default_rng(50 + chunk)
+    L, kv = [9, 5], [20, 5]
+    query, key, value, bt, _ = _case(rng, 2, L, kv, 4, 2, 6, 4)
+    o, l = oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CHUNKED_CAUSAL, 4, 2, 0.6,
+                                 chunk=chunk)
+    want = _brute_chunked(query, key, value, bt, L, kv, 4, 2, 0.6, chunk)
+    for (r, h), (wo, wl) in want.items():
+        np.testing.assert_allclose(o[r, h], wo, atol=1e-12)
+        assert abs(l[r, h] - wl) < 1e-12
+
+
+def test_chunked_mask_special_cases():
+    rng = np.random.default_rng(57)
+    L, kv = [12, 7], [30, 7]
+    query, key, value, bt, _ = _case(rng, 2, L, kv, 2, 2, 5, 4)
+    # a chunk at least as long as every sequence: plain causal
+    oc, lc = oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CHUNKED_CAUSAL, 2, 2, 0.7,
+                                   chunk=64)
+    ref, lref = oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CAUSAL, 2, 2, 0.7)
+    np.testing.assert_allclose(oc, ref, atol=1e-13)
+    np.testing.assert_allclose(lc, lref, atol=1e-13)
+    # chunk 1: every row sees only its own key -> that key's value, LSE = its score
+    o1, l1 = oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CHUNKED_CAUSAL, 2, 2, 0.7,
+                                   chunk=1)
+    row = 0
+    for b in range(2):
+        for i in range(L[b]):
+            a = kv[b] - L[b] + i
+            blk, slot = bt[b][a // 4], a % 4
+            for h in range(2):
+                np.testing.assert_allclose(o1[row + i, h], value[blk, slot, h], atol=1e-13)
+                s = float(np.float32(0.7)) * float(np.dot(query[row + i, h], key[blk, slot, h]))
+                assert abs(l1[row + i, h] - s) < 1e-12
+        row += L[b]
+    with pytest.raises(ValueError):
+        oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CHUNKED_CAUSAL, 2, 2, 0.7)

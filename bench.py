@@ -59,6 +59,15 @@ def prefill_valid_flops(seq_len, kv_seq_len, causal, head_num, head_size):
     return visible_pairs(seq_len, kv_seq_len, causal) * head_num * 4 * head_size
 
 
+def prefill_valid_flops_chunked(seq_len, kv_seq_len, chunk, head_num, head_size):
+    """Valid FLOPs of the chunked local causal mask: row a sees a - chunk*floor(a/chunk) + 1 keys."""
+    pairs = 0
+    for L, kv in zip(seq_len, kv_seq_len):
+        a = np.arange(int(kv) - int(L), int(kv), dtype=np.int64)
+        pairs += int((a - (a // chunk) * chunk + 1).sum())
+    return pairs * head_num * 4 * head_size
+
+
 def padding_positions(lengths, padded_to):
     """B * Lmax - sum L_i (padding count of a padded batch)."""
     return len(lengths) * int(padded_to) - int(np.sum(lengths))
@@ -383,6 +392,19 @@ def main():
             op.close()
             del c, op
             torch.cuda.empty_cache()
+        # chunked local causal mask over one 16384-token bf16 sequence, 40 heads, chunk 2048
+        print("bench: extra chunked_16384_c2048", file=sys.stderr, flush=True)
+        cc = W.make_prefill(87, np.array([16384]), np.array([16384]), 40, 40, 128, 128, "bf16", 9,
+                            1.0 / np.sqrt(128.0), chunk=2048).to(dev)
+        op = mpa.PrefixEncoder(cc.query, cc.key, cc.value, cc.block_tables, cc.seq_len, cc.kv_seq_len,
+                               mask_type=cc.mask_type, qk_scale=cc.qk_scale, return_lse=True,
+                               attention_chunk=cc.chunk)
+        ms = time_op(torch, op.run, 10, 3)
+        fl = prefill_valid_flops_chunked(cc.seq_len, cc.kv_seq_len, cc.chunk, cc.head_num, cc.head_size)
+        extra["chunked_16384_c2048"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                        "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+        op.close()
+        del cc, op
         print("bench: extra mla_spec_q4", file=sys.stderr, flush=True)
         m4 = W.make_mla_config("mla_spec_q4", device=dev)
         op4 = mpa.MLA(m4.q_nope, m4.q_rope, m4.ct_kv, m4.k_rope, m4.block_tables, m4.context_lens,

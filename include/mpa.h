@@ -117,6 +117,24 @@ mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
     const int64_t *qStartLoc, int64_t nTokens, void *attnOut, float *lse,
     uint64_t *workspaceSize, mpaOperation **op);
 
+/*
+ * PrefixEncoder, phase 1, with a chunked local causal mask (a library extension:
+ * the LLaMA 4 chunked attention of the page "终极指南：LLaMA模型的Transformer注意力掩码与
+ * 填充处理技术解析", section "本地注意力掩码生成").  With C = attentionChunkSize, row i
+ * of sequence b (absolute position a_i as above) sees the keys j with
+ *     j <= a_i  and  floor(j / C) == floor(a_i / C)
+ * (and j < kvSeqLen[b]); no bias.  The other arguments, outputs and errors are
+ * those of mpaSelfAttentionPrefixEncoderGetWorkspaceSize with maskType causal and
+ * no slopes; attentionChunkSize < 1 is MPA_ERROR_INVALID_ARG.  Phase 2 is
+ * mpaSelfAttentionPrefixEncoder.
+ */
+mpaStatus mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
+    const void *query, const void *key, const void *value, const int32_t *blockTables,
+    const int32_t *seqLen, const int32_t *kvSeqLen, int32_t attentionChunkSize, int32_t headNum,
+    int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks,
+    int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t *qStartLoc, int64_t nTokens,
+    void *attnOut, float *lse, uint64_t *workspaceSize, mpaOperation **op);
+
 /* PrefixEncoder, phase 2: launch on `stream` (hipStream_t).  `workspace` may be
  * NULL when the size phase 1 returned is 0. */
 mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,

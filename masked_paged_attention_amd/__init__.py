@@ -82,7 +82,9 @@ class PrefixEncoder:
 
     def __init__(self, query, key, value, block_tables, seq_len, kv_seq_len, *, mask_type,
                  qk_scale, slopes=None, q_start_loc=None, head_num=None, kv_head_num=None,
-                 out=None, lse=None, return_lse=False):
+                 out=None, lse=None, return_lse=False, attention_chunk=None):
+        """attention_chunk: chunk size of the chunked local causal mask (then
+        mask_type must be MASK_CAUSAL and slopes None)."""
         _need(query.is_cuda and key.is_cuda and value.is_cuda and block_tables.is_cuda,
               "query, key, value and block_tables must be device tensors")
         _need(query.dtype in _DTYPES and key.dtype == query.dtype and value.dtype == query.dtype,
@@ -126,12 +128,22 @@ class PrefixEncoder:
         self.device = query.device
         ws = ctypes.c_uint64(0)
         op = ctypes.c_void_p(0)
-        st = LIB.mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
-            _ptr(query), _ptr(key), _ptr(value), _ptr(block_tables), p_seq, p_kv, _ptr(slopes),
-            int(mask_type), H, kvh, float(qk_scale), B, D, nb, bs, block_tables.shape[1],
-            _DTYPES[query.dtype], p_qs, n_tokens, _ptr(self.out), _ptr(lse),
-            ctypes.byref(ws), ctypes.byref(op))
-        _check(st, "mpaSelfAttentionPrefixEncoderGetWorkspaceSize")
+        if attention_chunk is None:
+            st = LIB.mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
+                _ptr(query), _ptr(key), _ptr(value), _ptr(block_tables), p_seq, p_kv, _ptr(slopes),
+                int(mask_type), H, kvh, float(qk_scale), B, D, nb, bs, block_tables.shape[1],
+                _DTYPES[query.dtype], p_qs, n_tokens, _ptr(self.out), _ptr(lse),
+                ctypes.byref(ws), ctypes.byref(op))
+            _check(st, "mpaSelfAttentionPrefixEncoderGetWorkspaceSize")
+        else:
+            _need(int(mask_type) == MASK_CAUSAL and slopes is None,
+                  "the chunked local mask is causal and takes no slopes")
+            st = LIB.mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
+                _ptr(query), _ptr(key), _ptr(value), _ptr(block_tables), p_seq, p_kv, int(attention_chunk),
+                H, kvh, float(qk_scale), B, D, nb, bs, block_tables.shape[1],
+                _DTYPES[query.dtype], p_qs, n_tokens, _ptr(self.out), _ptr(lse),
+                ctypes.byref(ws), ctypes.byref(op))
+            _check(st, "mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize")
         self._op = op
         self.workspace = (torch.empty(ws.value, dtype=torch.uint8, device=query.device)
                           if ws.value else None)
@@ -157,13 +169,13 @@ class PrefixEncoder:
 
 def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, *,
                    mask_type=MASK_CAUSAL, qk_scale=None, slopes=None, q_start_loc=None,
-                   out=None, lse=None, return_lse=False, stream=None):
+                   out=None, lse=None, return_lse=False, stream=None, attention_chunk=None):
     """One masked paged-attention call; returns out, or (out, lse) with return_lse."""
     if qk_scale is None:
         qk_scale = 1.0 / float(query.shape[-1]) ** 0.5
     op = PrefixEncoder(query, key, value, block_tables, seq_len, kv_seq_len, mask_type=mask_type,
                        qk_scale=qk_scale, slopes=slopes, q_start_loc=q_start_loc, out=out, lse=lse,
-                       return_lse=return_lse)
+                       return_lse=return_lse, attention_chunk=attention_chunk)
     try:
         return op.run(stream)
     finally:

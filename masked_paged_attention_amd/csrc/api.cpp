@@ -49,6 +49,9 @@ int shift_of(int bs) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+// kernel mask type of the chunked local causal mask (selected through the
+// chunked entry point; not a PrefixEncoder maskType value)
+constexpr int kMaskChunkedCausal = 10;
 
 }  // namespace
 
@@ -188,21 +191,18 @@ mpaStatus mpaDestroyOperation(mpaOperation* op) {
   return MPA_OK;
 }
 
-mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
-    const void* query, const void* key, const void* value, const int32_t* blockTables,
-    const int32_t* seqLen, const int32_t* kvSeqLen, const float* slopes, int maskType,
-    int32_t headNum, int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
-    int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
-    int64_t nTokens, void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
-  g_last_error.clear();
-  if (op) *op = nullptr;
-  mpaStatus st = check_prefill(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType,
-                               headNum, kvHeadNum, qkScale, batch, headSize, numBlocks, blockSize,
-                               maxBlockNum, dtype, qStartLoc, nTokens, attnOut, workspaceSize, op);
-  if (st != MPA_OK) return st;
+namespace {
 
+// Phase 1 of the prefix encoder after validation; chunk > 0 selects the chunked
+// local causal mask (kernel mask 10).
+mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
+                          const int32_t* blockTables, const int32_t* seqLen, const int32_t* kvSeqLen,
+                          const float* slopes, int maskType, int32_t chunk, int32_t headNum,
+                          int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
+                          int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
+                          void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
   const bool causal = maskType != MPA_MASK_NONE;
-  mpa::PrefillPlan plan = mpa::plan_prefill(seqLen, kvSeqLen, batch, causal, headNum, kvHeadNum);
+  mpa::PrefillPlan plan = mpa::plan_prefill(seqLen, kvSeqLen, batch, causal, headNum, kvHeadNum, chunk);
   std::vector<int32_t> seqs(4 * (size_t)batch);
   int64_t packed = 0;
   for (int b = 0; b < batch; ++b) {
@@ -215,10 +215,11 @@ mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
   }
   mpaOperation* o = new (std::nothrow) mpaOperation();
   if (!o) return fail(MPA_ERROR_HIP, "out of host memory");
+  mpaStatus st;
   o->kind = mpaOperation::kPrefill;
   o->dtype = dtype;
   o->head_size = headSize;
-  o->mask_type = maskType;
+  o->mask_type = chunk > 0 ? kMaskChunkedCausal : maskType;
   o->grid = (int)plan.items.size();
   std::vector<size_t> offs;
   st = upload(o, {{plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem)},
@@ -244,10 +245,49 @@ mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
   p.bs_shift = shift_of(blockSize);
   p.max_blocks = maxBlockNum;
   p.heads_per_item = plan.heads_per_item;
+  p.chunk = chunk;
   p.scale2 = qkScale * kLog2e;
   *workspaceSize = 0;
   *op = o;
   return MPA_OK;
+}
+
+}  // namespace
+
+mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
+    const void* query, const void* key, const void* value, const int32_t* blockTables,
+    const int32_t* seqLen, const int32_t* kvSeqLen, const float* slopes, int maskType,
+    int32_t headNum, int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
+    int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
+    int64_t nTokens, void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  mpaStatus st = check_prefill(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType,
+                               headNum, kvHeadNum, qkScale, batch, headSize, numBlocks, blockSize,
+                               maxBlockNum, dtype, qStartLoc, nTokens, attnOut, workspaceSize, op);
+  if (st != MPA_OK) return st;
+  return make_prefill_op(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType, 0, headNum,
+                         kvHeadNum, qkScale, batch, headSize, blockSize, maxBlockNum, dtype, qStartLoc,
+                         attnOut, lse, workspaceSize, op);
+}
+
+mpaStatus mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
+    const void* query, const void* key, const void* value, const int32_t* blockTables,
+    const int32_t* seqLen, const int32_t* kvSeqLen, int32_t attentionChunkSize, int32_t headNum,
+    int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks,
+    int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc, int64_t nTokens,
+    void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  if (attentionChunkSize < 1)
+    return fail(MPA_ERROR_INVALID_ARG, "attentionChunkSize must be >= 1 (got %d)", attentionChunkSize);
+  mpaStatus st = check_prefill(query, key, value, blockTables, seqLen, kvSeqLen, nullptr, MPA_MASK_CAUSAL,
+                               headNum, kvHeadNum, qkScale, batch, headSize, numBlocks, blockSize,
+                               maxBlockNum, dtype, qStartLoc, nTokens, attnOut, workspaceSize, op);
+  if (st != MPA_OK) return st;
+  return make_prefill_op(query, key, value, blockTables, seqLen, kvSeqLen, nullptr, MPA_MASK_CAUSAL,
+                         attentionChunkSize, headNum, kvHeadNum, qkScale, batch, headSize, blockSize,
+                         maxBlockNum, dtype, qStartLoc, attnOut, lse, workspaceSize, op);
 }
 
 mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize, mpaOperation* op,

@@ -23,10 +23,11 @@ struct PrefillParams {
   int bs_shift;                // log2(blockSize) when a power of two, else -1
   int max_blocks;
   int heads_per_item;
+  int chunk;                   // chunk size of the chunked local mask (mask 10), else 0
   float scale2;                // qkScale * log2(e)
 };
 
-// dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9.
+// dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9, or 10 (chunked local causal).
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
                           int grid, hipStream_t stream);
 

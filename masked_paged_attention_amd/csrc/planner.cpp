@@ -22,7 +22,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batch, bool causal,
-                         int head_num, int kv_head_num) {
+                         int head_num, int kv_head_num, int chunk) {
   PrefillPlan plan;
   const int group = head_num / kv_head_num;
   // Heads of one KV group share a workgroup (and so every K/V tile it loads);
@@ -47,8 +47,9 @@ PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batc
           const int r_end = std::min(L, r0 + plan.rows_per_item);
           const int64_t keys = causal ? std::min<int64_t>(kv, (int64_t)prefix + r_end) : kv;
           const int n_tiles = (int)ceil_div(keys, kKeysPerTile);
+          const int t_lo = chunk > 0 ? (int)((((int64_t)prefix + r0) / chunk) * chunk / kKeysPerTile) : 0;
           g.items.push_back({b, h0, r0, n_tiles});
-          g.work += n_tiles;
+          g.work += n_tiles - t_lo;
         }
       }
       std::stable_sort(g.items.begin(), g.items.end(),

@@ -19,7 +19,7 @@ struct PrefillItem {
   int32_t b;        // sequence, or -1 for an empty slot (exits at once)
   int32_t head0;    // first query head of the workgroup
   int32_t row0;     // first query row (within the sequence)
-  int32_t n_tiles;  // key tiles the workgroup visits
+  int32_t n_tiles;  // key tiles up to the last one the workgroup visits
 };
 
 struct PrefillPlan {
@@ -36,8 +36,10 @@ struct PrefillPlan {
 // (sequence, KV head) groups are spread over XCDs greedily by work; inside an
 // XCD groups run one after another and each group's items longest first.
 // Slots left over by uneven XCD loads are filled with empty items.
+// chunk > 0: chunked local causal mask, an item's work starts at the tile of its
+// first row's chunk.
 PrefillPlan plan_prefill(const int32_t* seq_len, const int32_t* kv_len, int batch, bool causal,
-                         int head_num, int kv_head_num);
+                         int head_num, int kv_head_num, int chunk = 0);
 
 // MLA decode geometry: one workgroup (8 waves) covers 128 query rows -- the
 // (token, head) pairs of a sequence, token-major -- and walks key tiles of 32.

@@ -60,6 +60,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   constexpr bool kCausal = MASK != 0;
   constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
   constexpr bool kAlibiSqrt = MASK == 4;
+  constexpr bool kChunked = MASK == 10;     // causal inside chunks of p.chunk keys
   constexpr int NC = D / 16;                // 16-wide contraction chunks of QK^T
   constexpr int NDT = D / 32;               // 32-row tiles of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -101,6 +102,13 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
   const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
   const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+  // Chunked mask: row a sees keys from lo(a) = chunk * floor(a / chunk) on; the
+  // item starts at the tile of its first row's lo, a wave skips the tiles below
+  // its first row's lo, and a tile below its last row's lo needs the predicate.
+  auto chunk_lo = [&](int a) { return kChunked ? (a / p.chunk) * p.chunk : 0; };
+  const int t_lo = chunk_lo(prefix + row0) / kBN;
+  const int w_lo = chunk_lo(prefix + wrow0);
+  const int w_lo_last = chunk_lo(prefix + max(wrow0, w_rows_end - 1));
 
   // Q^T operand: lane l holds query row wrow0 + lq, dims 16c + 8g .. +8.
   V8 qreg[NC];
@@ -193,20 +201,20 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
   const float scale2 = p.scale2;
 
-  int blk_next = n_tiles > 1 ? tile_block(1) : 0;
-  load_tile(0, tile_block(0));
+  int blk_next = t_lo + 1 < n_tiles ? tile_block(t_lo + 1) : 0;
+  load_tile(t_lo * kBN, tile_block(t_lo));
   store_tile(0);
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t_lo; t < n_tiles; ++t) {
+    const int buf = (t - t_lo) & 1;
     const int j0 = t * kBN;
     if (t + 1 < n_tiles) {
       load_tile(j0 + kBN, blk_next);
       if (t + 2 < n_tiles) blk_next = tile_block(t + 2);
     }
 
-    if (w_active && j0 < w_keys) {
+    if (w_active && j0 < w_keys && j0 + kBN > w_lo) {
       // S^T = K Q^T for keys j0 .. j0+63 (two 32-key blocks).
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -223,7 +231,8 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
       const int dbase = a_lane - j0 - 4 * g;  // a - key at C = 0
       const int klim = kv - j0 - 4 * g;       // key < kv  <=>  C < klim
       const int vlim = kCausal ? min(klim, dbase + 1) : klim;
-      const bool partial = j0 + kBN > w_full_keys;
+      const int llim = chunk_lo(a_lane) - j0 - 4 * g;  // chunked: key >= lo(a)  <=>  C >= llim
+      const bool partial = j0 + kBN > w_full_keys || (kChunked && j0 < w_lo_last);
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
       const float dbf = (float)dbase;
       const float nbm = -slope2 * dbf - m_ref;  // linear ALiBi: slope2 * (C - dbase) - m_ref
@@ -244,7 +253,8 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
             } else {
               x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
             }
-            if constexpr (decltype(with_mask)::value) x = (C < vlim) ? x : -INFINITY;
+            if constexpr (decltype(with_mask)::value)
+              x = (C < vlim && (!kChunked || C >= llim)) ? x : -INFINITY;
             s[kb][r] = x;
             m = fmaxf(m, x);
           }
@@ -363,6 +373,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
   constexpr bool kAlibiSqrt = MASK == 4;
   constexpr bool kReverse = kAlibiLinear || kAlibiSqrt;
+  constexpr bool kChunked = MASK == 10;   // causal inside chunks of p.chunk keys
   constexpr int NC = D / 16;              // 16-wide contraction chunks of QK^T
   constexpr int NDT = D / 32;             // 32-row tiles of O^T
   constexpr int kRowBytes = D * (int)sizeof(T);   // 256
@@ -399,12 +410,19 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 
   const int item_rows_end = min(L, row0 + rows_per_item);
   const int wg_keys = kCausal ? min(kv, prefix + item_rows_end) : kv;
-  const int n_tiles = (wg_keys + kBN - 1) / kBN;
+  const int n_end = (wg_keys + kBN - 1) / kBN;
+  // Chunked mask: row a sees keys from lo(a) = chunk * floor(a / chunk) on; the
+  // item starts at the tile of its first row's lo.
+  auto chunk_lo = [&](int a) { return kChunked ? (a / p.chunk) * p.chunk : 0; };
+  const int t_lo = chunk_lo(prefix + row0) / kBN;
+  const int n_tiles = n_end - t_lo;  // iterations
   const bool w_active = wrow0 < L;
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
   const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
   const int w_tiles = w_active ? (w_keys + kBN - 1) / kBN : 0;  // tiles 0 .. w_tiles-1 matter here
   const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+  const int w_t_lo = chunk_lo(prefix + wrow0) / kBN;                       // first tile the wave sees
+  const int w_lo_last = chunk_lo(prefix + max(wrow0, w_rows_end - 1));   // below it: predicate
 
   // Q^T operand: lane l holds query row wrow0 + lq, dims 16c + 8g .. +8.
   V8 qreg[NC];
@@ -430,7 +448,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const int lrow = l >> 4;
   const unsigned lchunk16 = 16u * (unsigned)((l & 15) ^ (4 * lrow));
   const unsigned lds_base = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds;
-  auto tile_of = [&](int u) { return kReverse ? n_tiles - 1 - u : u; };
+  auto tile_of = [&](int u) { return kReverse ? n_tiles - 1 - u : t_lo + u; };
   auto block_of = [&](int u) -> int { return (u < n_tiles) ? btab[(tile_of(u) * kBN) >> p.bs_shift] : 0; };
   struct TileSrc {
     const char* k;
@@ -488,7 +506,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     const int dbase = a_lane - j0 - 4 * g;
     const int klim = kv - j0 - 4 * g;
     const int vlim = kCausal ? min(klim, dbase + 1) : klim;
-    const bool partial = j0 + kBN > w_full_keys;
+    const int llim = chunk_lo(a_lane) - j0 - 4 * g;  // chunked: key >= lo(a)  <=>  C >= llim
+    const bool partial = j0 + kBN > w_full_keys || (kChunked && j0 < w_lo_last);
     const float dbf = (float)dbase;
     float x[2][16];
     float psum;
@@ -533,7 +552,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           for (int r = 0; r < 16; ++r) {
             const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
             float v = score(kb, r, m_ref, nbm);
-            if constexpr (decltype(with_mask)::value) v = (C < vlim) ? v : -INFINITY;
+            if constexpr (decltype(with_mask)::value)
+              v = (C < vlim && (!kChunked || C >= llim)) ? v : -INFINITY;
             x[kb][r] = v;
             m = fmaxf(m, v);
           }
@@ -609,7 +629,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     auto issue_next = [&](int k) __attribute__((always_inline)) {
       if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
     };
-    if (t < w_tiles) {
+    if (t < w_tiles && t >= w_t_lo) {
       s[0] = f32x16{};
       s[1] = f32x16{};
 #pragma unroll
@@ -683,6 +703,7 @@ hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStrea
       case 4: hipLaunchKernelGGL((prefill_dma_kernel<T, 4>), g, blk, 0, s, p, p.block_tables); break;
       case 5: hipLaunchKernelGGL((prefill_dma_kernel<T, 5>), g, blk, 0, s, p, p.block_tables); break;
       case 9: hipLaunchKernelGGL((prefill_dma_kernel<T, 9>), g, blk, 0, s, p, p.block_tables); break;
+      case 10: hipLaunchKernelGGL((prefill_dma_kernel<T, 10>), g, blk, 0, s, p, p.block_tables); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -693,6 +714,7 @@ hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStrea
     case 4: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 4>), g, blk, 0, s, p); break;
     case 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 5>), g, blk, 0, s, p); break;
     case 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 9>), g, blk, 0, s, p); break;
+    case 10: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 10>), g, blk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -85,3 +85,14 @@ def test_short_kernel_name_of_the_dma_prefill_kernel():
     assert bench.short_kernel_name(
         "_ZN3mpa12_GLOBAL__N_118prefill_dma_kernelIDF16bLi9EEEvNS_13PrefillParamsEPKi") == \
         "prefill_dma_kernel<bf16,9>"
+
+
+def test_chunked_valid_flops_match_brute_force():
+    import bench
+    L, kv, C = [7, 5], [20, 5], 6
+    pairs = 0
+    for l_, k_ in zip(L, kv):
+        for i in range(l_):
+            a = k_ - l_ + i
+            pairs += sum(1 for j in range(k_) if j <= a and j // C == a // C)
+    assert bench.prefill_valid_flops_chunked(L, kv, C, 3, 64) == pairs * 3 * 4 * 64

@@ -162,3 +162,26 @@ def test_alibi_score_spikes_move_the_running_max(dtype, mask):
     c = c.to(DEV)
     out, lse = gpu_prefill(c)
     check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D,bs,chunk", [(128, 128, 64), (128, 128, 100), (128, 64, 256), (128, 24, 37),
+                                        (64, 16, 48)])
+def test_chunked_local_mask(dtype, D, bs, chunk):
+    # chunked local causal mask: row at absolute a sees keys j <= a of its own chunk
+    log(f"case chunked dtype={dtype} D={D} bs={bs} chunk={chunk}")
+    c = W.make_prefill(83 + chunk, np.array([300, 200, 17]), np.array([800, 200, 107]), 8, 2, D, bs, dtype,
+                       9, 1.0 / np.sqrt(D), poison=True, chunk=chunk,
+                       name=f"chunk{chunk}-{dtype}-D{D}-bs{bs}").to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+def test_chunked_mask_with_a_long_chunk_equals_causal():
+    log("case chunked (chunk >= kvSeqLen) equals causal")
+    c = W.make_prefill(85, np.array([260, 90]), np.array([700, 90]), 4, 4, 128, 128, "bf16", 9,
+                       1.0 / np.sqrt(128), poison=False, chunk=4096).to(DEV)
+    o1, l1 = gpu_prefill(c)
+    import dataclasses
+    o2, l2 = gpu_prefill(dataclasses.replace(c, chunk=0))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -95,6 +95,7 @@ class PrefillCase:
     key: torch.Tensor            # [numBlocks, blockSize, kvHeadNum, headSize]
     value: torch.Tensor
     block_tables: torch.Tensor   # int32 [B, maxBlockNum]
+    chunk: int = 0               # chunk size of the chunked local causal mask, 0: none
 
     @property
     def batch(self):
@@ -128,16 +129,20 @@ class PrefillCase:
             if t.dtype == torch.bfloat16:
                 t = t.float()
             return t.numpy()
+        # the chunked local causal mask is mask type 10 on the oracle side (the
+        # library selects it by its own entry point with causal maskType 9)
         return dict(query=npy(self.query), key=npy(self.key), value=npy(self.value),
                     block_tables=self.block_tables.cpu().numpy(), seq_len=self.seq_len,
-                    kv_seq_len=self.kv_seq_len, slopes=self.slopes, mask_type=self.mask_type,
+                    kv_seq_len=self.kv_seq_len, slopes=self.slopes,
+                    mask_type=10 if self.chunk else self.mask_type,
                     head_num=self.head_num, kv_head_num=self.kv_head_num,
-                    qk_scale=self.qk_scale, q_start_loc=self.q_start_loc)
+                    qk_scale=self.qk_scale, q_start_loc=self.q_start_loc,
+                    chunk=self.chunk if self.chunk else None)
 
 
 def make_prefill(seed, seq_len, kv_seq_len, head_num, kv_head_num, head_size, block_size,
                  dtype, mask_type, qk_scale, slopes=None, std=1.0, poison=False,
-                 pad_to=None, max_block_num=None, name="custom", seed_val=None):
+                 pad_to=None, max_block_num=None, name="custom", seed_val=None, chunk=0):
     """Build a PrefillCase with explicit lengths.
 
     ``pad_to``: lay the query rows out padded (row offset pad_to * b) and allocate
@@ -179,7 +184,7 @@ def make_prefill(seed, seq_len, kv_seq_len, head_num, kv_head_num, head_size, bl
                        head_num=head_num, kv_head_num=kv_head_num, head_size=head_size,
                        block_size=block_size, mask_type=mask_type, qk_scale=float(qk_scale),
                        slopes=slopes, q_start_loc=q_start, query=query, key=key, value=value,
-                       block_tables=torch.from_numpy(table))
+                       block_tables=torch.from_numpy(table), chunk=int(chunk))
 
 
 def pad_prefill_case(case, pad_to, seed, poison=False, device=None):

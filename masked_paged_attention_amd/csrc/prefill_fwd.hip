@@ -629,7 +629,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     auto issue_next = [&](int k) __attribute__((always_inline)) {
       if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
     };
-    if (t < w_tiles && t >= w_t_lo) {
+    if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
       s[0] = f32x16{};
       s[1] = f32x16{};
 #pragma unroll

@@ -392,6 +392,23 @@ def main():
             op.close()
             del c, op
             torch.cuda.empty_cache()
+        # the same calls reading the page's compressed mask tile instead of generating
+        # the mask (register-staged kernel; one global read per 4 scores)
+        for name, cfg in [("prefix_gqa_causal_norm_tile", None), ("alibi_right_4x4096_tile", "alibi_right_4x4096")]:
+            print(f"bench: extra {name}", file=sys.stderr, flush=True)
+            c = pc if cfg is None else W.make_prefill_config(cfg, device=dev)
+            tile = W.compressed_tile(c.mask_type, c.dtype).to(dev)
+            sl = torch.as_tensor(c.slopes, device=dev) if c.slopes is not None else None
+            op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
+                                   mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
+                                   q_start_loc=c.q_start_loc, return_lse=True, compressed_mask=tile)
+            ms = time_op(torch, op.run, 10, 3)
+            fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
+            extra[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+            op.close()
+            del c, op, tile
+            torch.cuda.empty_cache()
         # chunked local causal mask over one 16384-token bf16 sequence, 40 heads, chunk 2048
         print("bench: extra chunked_16384_c2048", file=sys.stderr, flush=True)
         cc = W.make_prefill(87, np.array([16384]), np.array([16384]), 40, 40, 128, 128, "bf16", 9,

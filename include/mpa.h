@@ -13,7 +13,8 @@
  *       already holds their prefix (ATB page "PrefixEncoder", parameter table);
  *       causal, right-aligned / sqrt / left-aligned ALiBi and padding masks are
  *       generated inside the kernel (ATB page "压缩mask", sections 开启方式 and
- *       约束说明) -- no mask tensor is ever read.
+ *       约束说明); a separate phase-1 call reads an explicit compressed mask
+ *       tile instead.
  *   mpaMLAGetWorkspaceSize / mpaMLA
  *       split-KV decode of multi-head latent attention: 576-wide query/key
  *       (qNope 512 + qRope 64), 512-wide latent value, one KV head (ATB page
@@ -134,6 +135,45 @@ mpaStatus mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
     int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks,
     int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t *qStartLoc, int64_t nTokens,
     void *attnOut, float *lse, uint64_t *workspaceSize, mpaOperation **op);
+
+/*
+ * PrefixEncoder, phase 1, with an explicit compressed mask tensor (ATB page
+ * "压缩mask", section 约束说明, and ATB page "PrefixEncoder", parameter table,
+ * row mask): the bias and the visibility inside the diagonal block come from
+ * `mask` instead of being generated.  Same computation, arguments, outputs and
+ * errors as mpaSelfAttentionPrefixEncoderGetWorkspaceSize, plus:
+ *
+ *   mask         dev  dtype, row-major [maskRows, maskCols], 16-byte aligned;
+ *                     read only.  maskType 9 (the compressed norm mask of RoPE
+ *                     models, which has causal semantics): [128, 128].
+ *                     maskType 3, 4, 5: [256, 256].  The [headNum, seqLen, 128]
+ *                     ALiBi form is MPA_ERROR_UNSUPPORTED, and so is maskType 0.
+ *
+ * Expansion, on a grid of 128 absolute positions (query a_i: block bq = a_i /
+ * 128, row r = a_i % 128; key j: block bk, column c = j % 128; dk = bq - bk):
+ * keys of a later block (dk < 0) and keys j >= kvSeqLen[b] are hidden, an
+ * entry of -inf hides its key, and otherwise
+ *   maskType 9:  bias 0 for dk >= 1, mask[r][c] for dk = 0;
+ *   maskType 3:  y = mask[r][c] for dk = 0, mask[128 + r][c] - 128 (dk - 1)
+ *                for dk >= 1; bias = slopes[h] * y;
+ *   maskType 4:  the same y, a distance (entries <= 0 or -inf); bias =
+ *                -slopes[h] * sqrt(-y);
+ *   maskType 5:  y = mask[r][c] (dk = 0) or mask[128 + r][c] (dk >= 1), plus
+ *                the key block origin 128 bk; bias = slopes[h] * y.
+ * With the tiles the page describes, as read here (norm: 0 on and below the
+ * diagonal, -inf above; right-aligned: col - row on and below the diagonal of
+ * the 256 x 256 tile, -inf above; left-aligned: col there) the result equals
+ * the generated mask of the same maskType.  A row whose tile hides every key
+ * gets out = 0 and lse = -inf.  Phase 2 is mpaSelfAttentionPrefixEncoder; the operation keeps the
+ * mask pointer, which must stay valid until the launches that use it end.
+ */
+mpaStatus mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
+    const void *query, const void *key, const void *value, const int32_t *blockTables,
+    const int32_t *seqLen, const int32_t *kvSeqLen, const void *mask, int32_t maskRows,
+    int32_t maskCols, const float *slopes, int maskType, int32_t headNum, int32_t kvHeadNum,
+    float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks, int32_t blockSize,
+    int32_t maxBlockNum, int dtype, const int64_t *qStartLoc, int64_t nTokens, void *attnOut,
+    float *lse, uint64_t *workspaceSize, mpaOperation **op);
 
 /* PrefixEncoder, phase 2: launch on `stream` (hipStream_t).  `workspace` may be
  * NULL when the size phase 1 returned is 0. */

@@ -82,9 +82,12 @@ class PrefixEncoder:
 
     def __init__(self, query, key, value, block_tables, seq_len, kv_seq_len, *, mask_type,
                  qk_scale, slopes=None, q_start_loc=None, head_num=None, kv_head_num=None,
-                 out=None, lse=None, return_lse=False, attention_chunk=None):
+                 out=None, lse=None, return_lse=False, attention_chunk=None, compressed_mask=None):
         """attention_chunk: chunk size of the chunked local causal mask (then
-        mask_type must be MASK_CAUSAL and slopes None)."""
+        mask_type must be MASK_CAUSAL and slopes None).  compressed_mask: an
+        explicit compressed mask tile on the device, query's dtype ([128, 128]
+        for MASK_CAUSAL, [256, 256] for the ALiBi types), read by the kernel in
+        place of the generated mask."""
         _need(query.is_cuda and key.is_cuda and value.is_cuda and block_tables.is_cuda,
               "query, key, value and block_tables must be device tensors")
         _need(query.dtype in _DTYPES and key.dtype == query.dtype and value.dtype == query.dtype,
@@ -128,7 +131,20 @@ class PrefixEncoder:
         self.device = query.device
         ws = ctypes.c_uint64(0)
         op = ctypes.c_void_p(0)
-        if attention_chunk is None:
+        if compressed_mask is not None:
+            _need(attention_chunk is None, "a compressed mask does not combine with attention_chunk")
+            _need(compressed_mask.is_cuda and compressed_mask.dtype == query.dtype
+                  and compressed_mask.dim() == 2 and compressed_mask.is_contiguous(),
+                  "compressed_mask must be a contiguous 2-D device tensor of query's dtype")
+            self._keep = self._keep + (compressed_mask,)
+            st = LIB.mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
+                _ptr(query), _ptr(key), _ptr(value), _ptr(block_tables), p_seq, p_kv,
+                _ptr(compressed_mask), compressed_mask.shape[0], compressed_mask.shape[1], _ptr(slopes),
+                int(mask_type), H, kvh, float(qk_scale), B, D, nb, bs, block_tables.shape[1],
+                _DTYPES[query.dtype], p_qs, n_tokens, _ptr(self.out), _ptr(lse),
+                ctypes.byref(ws), ctypes.byref(op))
+            _check(st, "mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize")
+        elif attention_chunk is None:
             st = LIB.mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
                 _ptr(query), _ptr(key), _ptr(value), _ptr(block_tables), p_seq, p_kv, _ptr(slopes),
                 int(mask_type), H, kvh, float(qk_scale), B, D, nb, bs, block_tables.shape[1],
@@ -169,13 +185,15 @@ class PrefixEncoder:
 
 def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, *,
                    mask_type=MASK_CAUSAL, qk_scale=None, slopes=None, q_start_loc=None,
-                   out=None, lse=None, return_lse=False, stream=None, attention_chunk=None):
+                   out=None, lse=None, return_lse=False, stream=None, attention_chunk=None,
+                   compressed_mask=None):
     """One masked paged-attention call; returns out, or (out, lse) with return_lse."""
     if qk_scale is None:
         qk_scale = 1.0 / float(query.shape[-1]) ** 0.5
     op = PrefixEncoder(query, key, value, block_tables, seq_len, kv_seq_len, mask_type=mask_type,
                        qk_scale=qk_scale, slopes=slopes, q_start_loc=q_start_loc, out=out, lse=lse,
-                       return_lse=return_lse, attention_chunk=attention_chunk)
+                       return_lse=return_lse, attention_chunk=attention_chunk,
+                       compressed_mask=compressed_mask)
     try:
         return op.run(stream)
     finally:

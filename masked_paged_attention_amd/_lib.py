@@ -29,6 +29,15 @@ SIGNATURES = {
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, headSize, numBlocks, blockSize, maxBlockNum
         ctypes.c_int, c_i64p, ctypes.c_int64,        # dtype, qStartLoc, nTokens
         c_vp, c_vp, c_u64p, c_opp]),                 # attnOut, lse, workspaceSize, op
+    "mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize": (ctypes.c_int32, [
+        c_vp, c_vp, c_vp, c_vp,                      # query, key, value, blockTables
+        c_i32p, c_i32p,                              # seqLen, kvSeqLen
+        c_vp, ctypes.c_int32, ctypes.c_int32,        # mask, maskRows, maskCols
+        c_vp, ctypes.c_int,                          # slopes, maskType
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float,  # headNum, kvHeadNum, qkScale
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, headSize, numBlocks, blockSize, maxBlockNum
+        ctypes.c_int, c_i64p, ctypes.c_int64,        # dtype, qStartLoc, nTokens
+        c_vp, c_vp, c_u64p, c_opp]),                 # attnOut, lse, workspaceSize, op
     "mpaSelfAttentionPrefixEncoder": (ctypes.c_int32, [c_vp, ctypes.c_uint64, c_vp, c_vp]),
     "mpaMLAGetWorkspaceSize": (ctypes.c_int32, [
         c_vp, c_vp, c_vp, c_vp, c_vp,                # qNope, qRope, ctKV, kRope, blockTables

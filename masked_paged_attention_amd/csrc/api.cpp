@@ -200,7 +200,8 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
                           const float* slopes, int maskType, int32_t chunk, int32_t headNum,
                           int32_t kvHeadNum, float qkScale, int32_t batch, int32_t headSize,
                           int32_t blockSize, int32_t maxBlockNum, int dtype, const int64_t* qStartLoc,
-                          void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op) {
+                          void* attnOut, float* lse, uint64_t* workspaceSize, mpaOperation** op,
+                          const void* mask = nullptr, int32_t maskStride = 0) {
   const bool causal = maskType != MPA_MASK_NONE;
   mpa::PrefillPlan plan = mpa::plan_prefill(seqLen, kvSeqLen, batch, causal, headNum, kvHeadNum, chunk);
   std::vector<int32_t> seqs(4 * (size_t)batch);
@@ -219,7 +220,7 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
   o->kind = mpaOperation::kPrefill;
   o->dtype = dtype;
   o->head_size = headSize;
-  o->mask_type = chunk > 0 ? kMaskChunkedCausal : maskType;
+  o->mask_type = chunk > 0 ? kMaskChunkedCausal : mask ? (maskType | mpa::kMaskTileFlag) : maskType;
   o->grid = (int)plan.items.size();
   std::vector<size_t> offs;
   st = upload(o, {{plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem)},
@@ -246,6 +247,8 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
   p.max_blocks = maxBlockNum;
   p.heads_per_item = plan.heads_per_item;
   p.chunk = chunk;
+  p.mask = mask;
+  p.mask_stride = maskStride;
   p.scale2 = qkScale * kLog2e;
   *workspaceSize = 0;
   *op = o;
@@ -288,6 +291,35 @@ mpaStatus mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
   return make_prefill_op(query, key, value, blockTables, seqLen, kvSeqLen, nullptr, MPA_MASK_CAUSAL,
                          attentionChunkSize, headNum, kvHeadNum, qkScale, batch, headSize, blockSize,
                          maxBlockNum, dtype, qStartLoc, attnOut, lse, workspaceSize, op);
+}
+
+mpaStatus mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
+    const void* query, const void* key, const void* value, const int32_t* blockTables,
+    const int32_t* seqLen, const int32_t* kvSeqLen, const void* mask, int32_t maskRows,
+    int32_t maskCols, const float* slopes, int maskType, int32_t headNum, int32_t kvHeadNum,
+    float qkScale, int32_t batch, int32_t headSize, int32_t numBlocks, int32_t blockSize,
+    int32_t maxBlockNum, int dtype, const int64_t* qStartLoc, int64_t nTokens, void* attnOut,
+    float* lse, uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  if (maskType == MPA_MASK_NONE)
+    return fail(MPA_ERROR_UNSUPPORTED, "maskType 0 has no compressed mask (3, 4, 5 or 9)");
+  mpaStatus st = check_prefill(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType,
+                               headNum, kvHeadNum, qkScale, batch, headSize, numBlocks, blockSize,
+                               maxBlockNum, dtype, qStartLoc, nTokens, attnOut, workspaceSize, op);
+  if (st != MPA_OK) return st;
+  if (!mask) return fail(MPA_ERROR_INVALID_ARG, "mask is required");
+  if ((reinterpret_cast<uintptr_t>(mask) & 15) != 0)
+    return fail(MPA_ERROR_INVALID_ARG, "mask must be 16-byte aligned");
+  const int edge = maskType == MPA_MASK_CAUSAL ? mpa::kMaskTile : 2 * mpa::kMaskTile;
+  if (maskRows != edge || maskCols != edge)
+    return fail(MPA_ERROR_UNSUPPORTED,
+                "maskType %d takes a [%d, %d] compressed mask (got [%d, %d]); the [headNum, seqLen, 128] "
+                "form is not supported",
+                maskType, edge, edge, maskRows, maskCols);
+  return make_prefill_op(query, key, value, blockTables, seqLen, kvSeqLen, slopes, maskType, 0, headNum,
+                         kvHeadNum, qkScale, batch, headSize, blockSize, maxBlockNum, dtype, qStartLoc,
+                         attnOut, lse, workspaceSize, op, mask, edge);
 }
 
 mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize, mpaOperation* op,

@@ -24,10 +24,18 @@ struct PrefillParams {
   int max_blocks;
   int heads_per_item;
   int chunk;                   // chunk size of the chunked local mask (mask 10), else 0
+  const void* mask;            // compressed mask tile (mask_type | kMaskTileFlag), else null
+  int mask_stride;             // elements per tile row (128 or 256)
   float scale2;                // qkScale * log2(e)
 };
 
-// dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9, or 10 (chunked local causal).
+// Kernel mask type of a compressed mask tile read from memory: maskType (3, 4, 5, 9)
+// | kMaskTileFlag; the tile grid is kMaskTile absolute positions.
+constexpr int kMaskTileFlag = 16;
+constexpr int kMaskTile = 128;
+
+// dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9, 10 (chunked local
+// causal), or 3/4/5/9 | kMaskTileFlag (compressed tile in p.mask).
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
                           int grid, hipStream_t stream);
 

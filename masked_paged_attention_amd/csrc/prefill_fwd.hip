@@ -9,7 +9,8 @@
 //   s_j = qkScale * q.k_j + bias(a, j) over visible keys j,  o = softmax(s) V,
 //   lse = ln sum_j exp(s_j).
 // Visibility and bias are generated in registers from (maskType, slopes,
-// seqLen, kvSeqLen); no mask tensor exists.
+// seqLen, kvSeqLen); the register-staged kernel can instead read them from an
+// explicit compressed mask tile (ATB page "压缩mask", section 约束说明).
 //
 // Shape of one workgroup (256 threads = 4 waves of 64):
 //   * each wave owns 32 query rows of one head; the heads of one KV group share
@@ -57,10 +58,12 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   using V4 = typename Vec<T>::x4;
   constexpr int KSTR = D + 8;   // K tile row stride (elements): conflict-free 16-byte row reads
   constexpr int VSTR = D + 32;  // V tile row stride: conflict-free transpose reads
-  constexpr bool kCausal = MASK != 0;
-  constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
-  constexpr bool kAlibiSqrt = MASK == 4;
-  constexpr bool kChunked = MASK == 10;     // causal inside chunks of p.chunk keys
+  constexpr int kType = MASK & 15;          // maskType (0, 3, 4, 5, 9) or 10 (chunked)
+  constexpr bool kTile = (MASK & kMaskTileFlag) != 0;  // bias read from a compressed tile
+  constexpr bool kCausal = kType != 0;
+  constexpr bool kAlibiLinear = kType == 3 || kType == 5;
+  constexpr bool kAlibiSqrt = kType == 4;
+  constexpr bool kChunked = kType == 10;    // causal inside chunks of p.chunk keys
   constexpr int NC = D / 16;                // 16-wide contraction chunks of QK^T
   constexpr int NDT = D / 32;               // 32-row tiles of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -95,13 +98,21 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
 
   // Keys the workgroup visits, keys this wave needs, and keys every row of the
   // wave sees (tiles below that need no predicate).
+  // With a compressed tile the diagonal 128-block of a row is read whole (the
+  // tile decides which of its keys are visible), so the keys run to the end of
+  // the last row's block; every tile then takes the per-element predicate.
+  auto keys_to = [&](int rows_end) {
+    if constexpr (!kCausal) return kv;
+    const int a_last = prefix + rows_end - 1;
+    return kTile ? min(kv, (a_last / kMaskTile + 1) * kMaskTile) : min(kv, a_last + 1);
+  };
   const int item_rows_end = min(L, row0 + rows_per_item);
-  const int wg_keys = kCausal ? min(kv, prefix + item_rows_end) : kv;
+  const int wg_keys = keys_to(item_rows_end);
   const int n_tiles = (wg_keys + kBN - 1) / kBN;
   const bool w_active = wrow0 < L;
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
-  const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
-  const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+  const int w_keys = keys_to(w_rows_end);
+  const int w_full_keys = kTile ? 0 : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
   // Chunked mask: row a sees keys from lo(a) = chunk * floor(a / chunk) on; the
   // item starts at the tile of its first row's lo, a wave skips the tiles below
   // its first row's lo, and a tile below its last row's lo needs the predicate.
@@ -206,9 +217,38 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   store_tile(0);
   __syncthreads();
 
+  // Compressed tile (row-major, p.mask_stride elements per row) on a grid of
+  // kMaskTile absolute positions: query block bq = a / 128, in-block row r; key
+  // block bk, in-block column c; dk = bq - bk.  Keys of later blocks (dk < 0) are
+  // hidden.  Norm tile [128,128]: a key dk >= 1 blocks behind gets 0, one in the
+  // diagonal block tile[r][c].  ALiBi tiles [256,256]: the diagonal block reads
+  // row r, a key dk >= 1 blocks behind row 128 + r; the right-aligned bias
+  // (linear and sqrt) then moves by -128 per block beyond the first, the
+  // left-aligned one adds the key block origin 128 bk, applied here relative to
+  // the query block origin (-128 dk) with 128 bq slope moved into the LSE.  A -inf
+  // entry hides its key.
+  const int a_bq = a_lane / kMaskTile;
+  const T* mrow_diag = nullptr;
+  const T* mrow_back = nullptr;
+  if constexpr (kTile) {
+    const int r = a_lane - a_bq * kMaskTile;
+    mrow_diag = (const T*)p.mask + (long long)r * p.mask_stride + 4 * g;
+    mrow_back = kType == 9 ? mrow_diag : mrow_diag + (long long)kMaskTile * p.mask_stride;
+  }
+
   for (int t = t_lo; t < n_tiles; ++t) {
     const int buf = (t - t_lo) & 1;
     const int j0 = t * kBN;
+    // Tile entries of this lane's 32 keys: 8 runs of 4 (issued before the next
+    // K/V tile so that waiting on them leaves those loads in flight).
+    V4 mv[8];
+    int dk = 0;
+    if constexpr (kTile) {
+      dk = a_bq - j0 / kMaskTile;
+      const T* src = (dk == 0 ? mrow_diag : mrow_back) + (j0 & (kMaskTile - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mv[u] = *(const V4*)(src + 8 * u);
+    }
     if (t + 1 < n_tiles) {
       load_tile(j0 + kBN, blk_next);
       if (t + 2 < n_tiles) blk_next = tile_block(t + 2);
@@ -230,7 +270,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
       // domain), so that the exponent needs no further subtraction.
       const int dbase = a_lane - j0 - 4 * g;  // a - key at C = 0
       const int klim = kv - j0 - 4 * g;       // key < kv  <=>  C < klim
-      const int vlim = kCausal ? min(klim, dbase + 1) : klim;
+      const int vlim = kCausal && !kTile ? min(klim, dbase + 1) : klim;
       const int llim = chunk_lo(a_lane) - j0 - 4 * g;  // chunked: key >= lo(a)  <=>  C >= llim
       const bool partial = j0 + kBN > w_full_keys || (kChunked && j0 < w_lo_last);
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
@@ -246,7 +286,22 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
           for (int r = 0; r < 16; ++r) {
             const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
             float x;
-            if constexpr (kAlibiLinear) {
+            if constexpr (kTile) {
+              const float mval = (float)mv[4 * kb + (r >> 2)][r & 3];
+              bool hide = dk < 0 || mval == -INFINITY;
+              float bias2;  // bias in log2 units
+              if constexpr (kType == 9) {
+                bias2 = dk > 0 ? 0.0f : mval * kLog2e;
+                hide = dk < 0 || (dk == 0 && mval == -INFINITY);
+              } else if constexpr (kType == 5) {
+                bias2 = slope2 * (mval - (float)(kMaskTile * dk));
+              } else {
+                const float y = dk > 0 ? mval - (float)(kMaskTile * (dk - 1)) : mval;
+                bias2 = kAlibiSqrt ? -slope2 * fast_sqrt(-y) : slope2 * y;
+              }
+              x = __builtin_fmaf(s[kb][r], scale2, bias2 - m_ref);
+              x = hide ? -INFINITY : x;
+            } else if constexpr (kAlibiLinear) {
               x = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
             } else if constexpr (kAlibiSqrt) {
               x = __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
@@ -326,7 +381,8 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   const float l_tot = sum_with_other_half(l_run);
   const int i = wrow0 + lq;
   if (i >= L) return;
-  const float inv = 1.0f / l_tot;
+  // A row whose tile hides every key gets O = 0 (and LSE = -inf).
+  const float inv = kTile && l_tot == 0.0f ? 0.0f : 1.0f / l_tot;
   T* orow = (T*)p.out + (qs + i) * q_row_stride + (long long)head * D + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -340,7 +396,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   }
   if (p.lse != nullptr && g == 0) {
     float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if constexpr (MASK == 5) lse += p.slopes[head] * (float)a_lane;
+    if constexpr (kType == 5) lse += p.slopes[head] * (float)(kTile ? a_bq * kMaskTile : a_lane);
     p.lse[(qs + i) * p.head_num + head] = lse;
   }
 }
@@ -696,7 +752,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
-  if (D == 128 && p.bs_shift >= 6) {
+  if (D == 128 && p.bs_shift >= 6 && (mask_type & kMaskTileFlag) == 0) {
     switch (mask_type) {
       case 0: hipLaunchKernelGGL((prefill_dma_kernel<T, 0>), g, blk, 0, s, p, p.block_tables); break;
       case 3: hipLaunchKernelGGL((prefill_dma_kernel<T, 3>), g, blk, 0, s, p, p.block_tables); break;
@@ -715,6 +771,10 @@ hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStrea
     case 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 5>), g, blk, 0, s, p); break;
     case 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 9>), g, blk, 0, s, p); break;
     case 10: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 10>), g, blk, 0, s, p); break;
+    case kMaskTileFlag | 3: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 3>), g, blk, 0, s, p); break;
+    case kMaskTileFlag | 4: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 4>), g, blk, 0, s, p); break;
+    case kMaskTileFlag | 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 5>), g, blk, 0, s, p); break;
+    case kMaskTileFlag | 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 9>), g, blk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -129,8 +129,12 @@ def _check_prefix_args(seq_len, kv_seq_len, head_num, kv_head_num, mask_type, sl
 
 def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
                         slopes, mask_type, head_num, kv_head_num, qk_scale,
-                        rows, q_start_loc=None, chunk=None):
+                        rows, q_start_loc=None, chunk=None, mask_tile=None):
     """Oracle output for selected (b, i, h) triples only.
+
+    ``mask_tile``: an explicit compressed mask (ATB page "压缩mask", section
+    约束说明) whose expansion gives the bias and visibility in place of the
+    full rule of ``mask_type``.
 
     ``rows`` is an iterable of (b, i, h) with 0 <= i < seq_len[b].  Returns
     (O [n, D] fp64, LSE [n] fp64) in the order given.  Rows of the same (b, h) are
@@ -163,8 +167,11 @@ def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
             sel = ii[c0:c0 + ROW_CHUNK]
             a = (kv - L) + sel[:, None]
             j = np.arange(kv)[None, :]
-            vis = _m.visible(mask_type, a, j, kv, chunk)
-            msk = np.where(vis, _m.bias(mask_type, slope, a, j), -np.inf)
+            if mask_tile is not None:
+                msk = _m.compressed_bias(mask_type, mask_tile, slope, a, j, kv)
+            else:
+                vis = _m.visible(mask_type, a, j, kv, chunk)
+                msk = np.where(vis, _m.bias(mask_type, slope, a, j), -np.inf)
             q = np.asarray(query[starts[b] + sel, h, :], dtype=np.float64)
             o, ls = attend(q, k_all, v_all, scale, msk)
             out[idx[c0:c0 + ROW_CHUNK]] = o
@@ -174,8 +181,9 @@ def prefix_encoder_rows(query, key, value, block_tables, seq_len, kv_seq_len,
 
 def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, slopes,
                    mask_type, head_num, kv_head_num, qk_scale, q_start_loc=None,
-                   heads=None, chunk=None):
-    """Full oracle of the PrefixEncoder operation.
+                   heads=None, chunk=None, mask_tile=None):
+    """Full oracle of the PrefixEncoder operation (``mask_tile``: see
+    ``prefix_encoder_rows``).
 
     Returns (O [nTokens, headNum, D] fp64, LSE [nTokens, headNum] fp64).  Rows that
     belong to no sequence (padding rows of a padded layout) are NaN: they are not
@@ -196,7 +204,8 @@ def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, slopes,
             rows = [(b, i, h) for i in range(L)]
             o, ls = prefix_encoder_rows(query, key, value, block_tables, seq_len,
                                         kv_seq_len, slopes, mask_type, head_num,
-                                        kv_head_num, qk_scale, rows, q_start_loc, chunk)
+                                        kv_head_num, qk_scale, rows, q_start_loc, chunk,
+                                        mask_tile)
             out[starts[b]:starts[b] + L, h] = o
             lse[starts[b]:starts[b] + L, h] = ls
     return out, lse

@@ -151,29 +151,31 @@ def compressed_alibi_left():
     return np.where(y <= x, y.astype(np.float64), -np.inf)
 
 
-def expand_compressed(mask_type, tile, slope, seq_len, kv_len):
-    """Expand a compressed tile to the full [seq_len, kv_len] additive mask.
+def compressed_bias(mask_type, tile, slope, a, j, kv_len):
+    """Additive mask of the pairs (a, j) read from a compressed tile: the bias,
+    or -inf where the pair is hidden.  ``a`` (absolute query positions) and ``j``
+    (key positions) broadcast against each other.
 
     ``tile`` is what ``compressed_norm`` / ``compressed_alibi`` /
-    ``compressed_alibi_left`` return (the sqrt type uses the ``compressed_alibi``
-    tile in distance form).  Keys at or beyond kv_len are masked (padding).
+    ``compressed_alibi_left`` return, or any tile of the same shape (the sqrt
+    type uses the ``compressed_alibi`` tile in distance form).  Keys at or beyond
+    kv_len are masked (padding).
     """
-    prefix = kv_len - seq_len
-    a = prefix + np.arange(seq_len)[:, None]
-    j = np.arange(kv_len)[None, :]
+    a = np.asarray(a)
+    j = np.asarray(j)
+    shape = np.broadcast(a, j).shape
+    tile = np.asarray(tile, dtype=np.float64)
     bq, r = a // TILE, a % TILE
     bk, c = j // TILE, j % TILE
     k = bq - bk
-    out = np.full((seq_len, kv_len), -np.inf)
     if mask_type in (MASK_CAUSAL,):
         assert tile.shape == (TILE, TILE)
-        diag = tile[np.broadcast_to(r, out.shape), np.broadcast_to(c, out.shape)]
+        diag = tile[np.broadcast_to(r, shape), np.broadcast_to(c, shape)]
         out = np.where(k > 0, 0.0, np.where(k == 0, diag, -np.inf))
     elif mask_type in (MASK_ALIBI, MASK_ALIBI_SQRT):
         assert tile.shape == (2 * TILE, 2 * TILE)
-        rows = np.where(k == 0, r, TILE + r)
-        rows = np.broadcast_to(rows, out.shape)
-        cols = np.broadcast_to(c, out.shape)
+        rows = np.broadcast_to(np.where(k == 0, r, TILE + r), shape)
+        cols = np.broadcast_to(c, shape)
         val = tile[rows, cols]
         # A key k >= 1 tiles behind reuses the second band, shifted by 128 per
         # extra tile of distance.
@@ -183,11 +185,13 @@ def expand_compressed(mask_type, tile, slope, seq_len, kv_len):
             out = np.where(np.isfinite(val), slope * val, -np.inf)
         else:
             dist = -val
-            out = np.where(np.isfinite(val), -slope * np.sqrt(np.where(np.isfinite(dist), dist, 0.0)), -np.inf)
+            with np.errstate(invalid="ignore"):
+                out = np.where(np.isfinite(val), -slope * np.sqrt(np.where(np.isfinite(dist), dist, 0.0)),
+                               -np.inf)
     elif mask_type == MASK_ALIBI_LEFT:
         assert tile.shape == (2 * TILE, 2 * TILE)
-        rows = np.broadcast_to(np.where(k == 0, r, TILE + r), out.shape)
-        cols = np.broadcast_to(c, out.shape)
+        rows = np.broadcast_to(np.where(k == 0, r, TILE + r), shape)
+        cols = np.broadcast_to(c, shape)
         val = tile[rows, cols]
         # The tile holds the in-tile column; the key tile's origin is added back.
         val = np.where(k >= 0, val + TILE * bk, -np.inf)
@@ -195,3 +199,12 @@ def expand_compressed(mask_type, tile, slope, seq_len, kv_len):
     else:
         raise ValueError(f"mask type {mask_type} has no compressed form")
     return np.where(j < kv_len, out, -np.inf)
+
+
+def expand_compressed(mask_type, tile, slope, seq_len, kv_len):
+    """Expand a compressed tile to the full [seq_len, kv_len] additive mask
+    (rows at absolute positions kv_len - seq_len + i, see ``compressed_bias``)."""
+    prefix = kv_len - seq_len
+    a = prefix + np.arange(seq_len)[:, None]
+    j = np.arange(kv_len)[None, :]
+    return compressed_bias(mask_type, tile, slope, a, j, kv_len)

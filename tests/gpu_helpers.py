@@ -33,7 +33,8 @@ def gpu_prefill(case, return_lse=True, sentinel=None):
     mpa.prefix_encoder(case.query, case.key, case.value, case.block_tables, case.seq_len,
                        case.kv_seq_len, mask_type=case.mask_type, qk_scale=case.qk_scale,
                        slopes=slopes, q_start_loc=case.q_start_loc, out=out, lse=lse,
-                       attention_chunk=case.chunk if case.chunk else None)
+                       attention_chunk=case.chunk if case.chunk else None,
+                       compressed_mask=case.mask_tile)
     torch.cuda.synchronize()
     return out, lse
 

@@ -292,3 +292,39 @@ def test_lse_merge_validation(lib, kw):
 def test_lse_merge_zero_rows_is_a_no_op(lib):
     assert _merge(lib, rows=0) == 0, lib.mpaGetLastErrorMessage()
     assert _merge(lib, rows=0, o=0, l=0, out=0, lse=0) == 0, lib.mpaGetLastErrorMessage()
+
+
+def _prefill_tile(lib, tile=0x10000, rows=128, cols=128, mask=9, slopes=None):
+    seq, ps = _i32([4, 7])
+    kv, pk = _i32([4, 9])
+    ws = ctypes.c_uint64(123)
+    op = ctypes.c_void_p(0xdead)
+    st = lib.mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
+        FAKE, FAKE, FAKE, FAKE, ps, pk, ctypes.c_void_p(tile), rows, cols, slopes, mask,
+        4, 2, 0.125, 2, 64, 8, 16, 2, 0, ctypes.POINTER(ctypes.c_int64)(), 11, FAKE, None,
+        ctypes.byref(ws), ctypes.byref(op))
+    return st, op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tile=0), 1),                               # no mask
+    (dict(tile=0x10008), 1),                         # not 16-byte aligned
+    (dict(rows=256, cols=256), 2),                   # norm mask is [128, 128]
+    (dict(mask=3, slopes=FAKE), 2),                  # ALiBi takes [256, 256]
+    (dict(mask=4, slopes=FAKE, rows=256, cols=128), 2),  # [headNum, seqLen, 128] form: unsupported
+    (dict(mask=0), 2),                               # no compressed form
+    (dict(mask=5, rows=256, cols=256), 1),           # ALiBi without slopes
+])
+def test_compressed_mask_validation(lib, kw, status):
+    st, op = _prefill_tile(lib, **kw)
+    assert st == status, lib.mpaGetLastErrorMessage()
+    assert op.value is None or op.value == 0
+    assert lib.mpaGetLastErrorMessage()
+
+
+def test_compressed_mask_valid_args_reach_hip_or_succeed(lib):
+    for kw in (dict(), dict(mask=4, slopes=FAKE, rows=256, cols=256)):
+        st, op = _prefill_tile(lib, **kw)
+        assert st in (0, 4), lib.mpaGetLastErrorMessage()
+        if st == 0:
+            assert lib.mpaDestroyOperation(op) == 0

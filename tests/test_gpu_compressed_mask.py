@@ -1,0 +1,81 @@
+"""GPU parity of the PrefixEncoder call that reads an explicit compressed mask
+(ATB page "压缩mask", section 约束说明; ATB page "PrefixEncoder", parameter table,
+row mask) against the fp64 oracle's expansion of the same tile.
+
+The tiles are inputs (workloads.gen.compressed_tile): the page's tiles as read
+here (lower-triangular 0 / -inf norm mask, right-aligned col - row and
+left-aligned col below the diagonal), and perturbed copies (extra bias, holes of
+-inf) so that the kernel has to read every entry it uses.  Both sides get the same tile values
+after the cast to the input type."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads.gen as W
+from tests.gpu_helpers import check_prefill_full, gpu_prefill, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+CASES = [
+    # (seq_len, kv_seq_len, head_num, kv_head_num, D, bs): prefixes that start inside,
+    # at and across 128-position blocks, ragged ends, an empty sequence
+    ([300, 1, 0, 129], [700, 128, 5, 129], 8, 2, 128, 128),
+    ([200, 77], [457, 333], 4, 4, 64, 16),
+    ([256, 40], [256, 300], 4, 1, 128, 24),
+]
+
+
+@pytest.mark.parametrize("mask_type", [9, 3, 4, 5])
+@pytest.mark.parametrize("perturbed", [False, True])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_compressed_mask_matches_oracle(mask_type, perturbed, dtype, ci):
+    L, kv, H, KVH, D, bs = CASES[ci]
+    log(f"case compressed mask={mask_type} perturbed={perturbed} dtype={dtype} case={ci}")
+    slopes = "alibi" if mask_type != 9 else None
+    c = W.make_prefill(211 + ci, np.array(L), np.array(kv), H, KVH, D, bs, dtype, mask_type,
+                       1.0 / np.sqrt(D), slopes=slopes, poison=True,
+                       name=f"tile{mask_type}-{'pert' if perturbed else 'page'}-{dtype}-c{ci}")
+    c = dataclasses.replace(c, mask_tile=W.compressed_tile(mask_type, dtype, 17 + ci if perturbed else None))
+    c = c.to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("mask_type", [9, 3, 4, 5])
+def test_page_tile_equals_generated_mask(mask_type):
+    # the page's tile gives the result of the generated mask of the same type (both
+    # paths checked against one oracle, the generated one without any tile)
+    log(f"case compressed page tile vs generated mask={mask_type}")
+    slopes = "alibi" if mask_type != 9 else None
+    c = W.make_prefill(230, np.array([390, 130]), np.array([1000, 130]), 4, 2, 128, 128, "bf16", mask_type,
+                       1.0 / np.sqrt(128), slopes=slopes, poison=True, name=f"gen{mask_type}").to(DEV)
+    o_gen, l_gen = gpu_prefill(c)
+    check_prefill_full(c, o_gen, l_gen)
+    ct = dataclasses.replace(c, mask_tile=W.compressed_tile(mask_type, "bf16").to(DEV))
+    o_tile, l_tile = gpu_prefill(ct)
+    check_prefill_full(c, o_tile, l_tile)
+
+
+def test_row_hidden_by_the_tile_is_zero():
+    # a norm tile whose row 5 is all -inf: query position 5 (no prefix) sees nothing
+    log("case compressed norm tile with an empty row")
+    tile = W.compressed_tile(9, "fp16")
+    tile[5, :] = float("-inf")
+    c = W.make_prefill(240, np.array([40]), np.array([40]), 2, 2, 64, 16, "fp16", 9, 0.125,
+                       poison=True, name="empty-row")
+    c = dataclasses.replace(c, mask_tile=tile).to(DEV)
+    out, lse = gpu_prefill(c)
+    assert torch.all(out[5] == 0)
+    assert torch.all(torch.isneginf(lse[5]))
+    keep = torch.ones(40, dtype=torch.bool)
+    keep[5] = False
+    import oracle
+    ro, rl = oracle.prefix_encoder(**c.oracle_args())
+    assert np.abs(out[keep].float().cpu().numpy() - ro[keep.numpy()]).max() <= 5e-3
+    assert np.all(np.isneginf(rl[5]))

@@ -2,7 +2,8 @@
 
 This package only draws random numbers and lays them out in the operator's
 layouts (packed / padded query rows, paged key/value cache with a random block
-permutation, block tables, host length arrays, ALiBi slopes).  It holds none of
+permutation, block tables, host length arrays, ALiBi slopes, explicit compressed
+mask tiles).  It holds none of
 the attention arithmetic: both the HIP path's tests/benchmark and the fp64 oracle
 read the tensors it returns.
 """
@@ -13,6 +14,7 @@ from .gen import (  # noqa: F401
     PrefillCase,
     MLACase,
     alibi_slopes,
+    compressed_tile,
     make_prefill,
     make_prefill_config,
     make_mla,

@@ -96,6 +96,7 @@ class PrefillCase:
     value: torch.Tensor
     block_tables: torch.Tensor   # int32 [B, maxBlockNum]
     chunk: int = 0               # chunk size of the chunked local causal mask, 0: none
+    mask_tile: Optional[torch.Tensor] = None  # explicit compressed mask ([128,128] / [256,256]), dtype
 
     @property
     def batch(self):
@@ -120,7 +121,8 @@ class PrefillCase:
 
     def to(self, device):
         return replace(self, query=self.query.to(device), key=self.key.to(device),
-                       value=self.value.to(device), block_tables=self.block_tables.to(device))
+                       value=self.value.to(device), block_tables=self.block_tables.to(device),
+                       mask_tile=None if self.mask_tile is None else self.mask_tile.to(device))
 
     def oracle_args(self):
         """Numpy views of the same values (fp16 stays fp16; bf16 is widened to fp32 exactly)."""
@@ -137,7 +139,37 @@ class PrefillCase:
                     mask_type=10 if self.chunk else self.mask_type,
                     head_num=self.head_num, kv_head_num=self.kv_head_num,
                     qk_scale=self.qk_scale, q_start_loc=self.q_start_loc,
-                    chunk=self.chunk if self.chunk else None)
+                    chunk=self.chunk if self.chunk else None,
+                    mask_tile=None if self.mask_tile is None else npy(self.mask_tile).astype(np.float64))
+
+
+def compressed_tile(mask_type, dtype, seed=None):
+    """An explicit compressed mask tile as the ATB page "压缩mask" (section 约束说明)
+    describes it, in the reading used throughout: [128,128] norm (0 on and below
+    the diagonal, -inf above) for the causal type; [256,256] with col - row
+    (right-aligned ALiBi, linear and sqrt) or col (left-aligned) on and below the
+    diagonal, -inf above.  With ``seed``, a perturbed copy: an extra bias in steps
+    of 1/4 (kept <= 0 for the right-aligned distance form) and -inf holes in about
+    3% of the entries below the diagonal, so that every entry a call reads
+    matters.  Returned on the CPU in the input type."""
+    n = 128 if mask_type == MASK_CAUSAL else 256
+    r = torch.arange(n, dtype=torch.float32)[:, None]
+    c = torch.arange(n, dtype=torch.float32)[None, :]
+    below = c <= r
+    if mask_type == MASK_CAUSAL:
+        val = torch.zeros(n, n)
+    elif mask_type in (MASK_ALIBI, MASK_ALIBI_SQRT):
+        val = c - r
+    elif mask_type == MASK_ALIBI_LEFT:
+        val = c.expand(n, n).clone()
+    else:
+        raise ValueError(f"mask type {mask_type} has no compressed tile")
+    if seed is not None:
+        g = torch.Generator("cpu").manual_seed(seed)
+        hi = {MASK_CAUSAL: 9, MASK_ALIBI: 1, MASK_ALIBI_SQRT: 1, MASK_ALIBI_LEFT: 13}[mask_type]
+        val = val + torch.randint(-12, hi, (n, n), generator=g).float() / 4
+        below = below & ~((torch.rand(n, n, generator=g) < 0.03) & (c < r))
+    return torch.where(below, val, torch.tensor(float("-inf"))).to(TORCH_DTYPE[dtype]).contiguous()
 
 
 def make_prefill(seed, seq_len, kv_seq_len, head_num, kv_head_num, head_size, block_size,

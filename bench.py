@@ -84,6 +84,18 @@ def mla_bytes(context_lens, q_tokens, head_num, elem=2, with_lse=True, max_block
     return kv + q + o + lse + bt
 
 
+def mla_bytes_int8(context_lens, q_tokens, head_num, elem=2, max_blocks=None):
+    """Algorithmic HBM bytes of one MLA call over the int8 latent cache: every
+    latent row once (512 int8 + 64 rope values), the query (512 int8 + 64), the
+    output (512), the LSE (fp32), the block table and the two per-head descales."""
+    kv = int(np.sum(context_lens)) * (512 + 64 * elem)
+    q = q_tokens * head_num * (512 + 64 * elem)
+    o = q_tokens * head_num * 512 * elem
+    lse = q_tokens * head_num * 4
+    bt = len(context_lens) * (max_blocks or 0) * 4
+    return kv + q + o + lse + bt + 2 * head_num * 4
+
+
 def mla_flops(context_lens, q_seq_len, head_num, spec):
     """2*576 + 2*512 flops per visible (token, key) pair per head."""
     pairs = 0
@@ -449,6 +461,33 @@ def main():
                                 "shape": "4 x 256 tokens, ctx 1024..4096, 128 heads, causal"}
         opp.close()
         del mp, opp
+        # MLA decode over the int8 latent cache, the decode workload's shape; two
+        # caches alternate (2 x 189 MB > the 256 MB Infinity Cache).
+        print("bench: extra mla_int8_decode_q1", file=sys.stderr, flush=True)
+        rng8 = np.random.default_rng(1001)
+        ctx8 = rng8.integers(1024, 8192, size=64, endpoint=True)
+        m8 = [W.make_mla_int8(3101 + i, ctx8, None, 128, 128, "bf16", 0, 0, 1.0 / np.sqrt(192.0),
+                              max_block_num=64).to(dev) for i in range(2)]
+        o8 = torch.empty((m8[0].n_tokens, 128, 512), dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty((m8[0].n_tokens, 128), dtype=torch.float32, device=dev)
+        ops8 = [mpa.MLA(m.q_nope, m.q_rope, m.ct_kv, m.k_rope, m.block_tables, m.context_lens,
+                        qk_scale=m.qk_scale, out=o8, lse=l8,
+                        qk_descale=torch.as_tensor(m.qk_descale, device=dev),
+                        pv_descale=torch.as_tensor(m.pv_descale, device=dev)) for m in m8]
+        flip = [0]
+
+        def run8():
+            ops8[flip[0]].run()
+            flip[0] ^= 1
+        ms = time_op(torch, run8, 20, 4)
+        by = mla_bytes_int8(ctx8, m8[0].n_tokens, 128, max_blocks=64)
+        fl = mla_flops(ctx8, None, 128, False)
+        extra["mla_int8_decode_q1"] = {"ms": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                                       "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1), "bytes": by}
+        for op8 in ops8:
+            op8.close()
+        del m8, ops8, o8, l8
         # LSE merge of 8 partials shaped like the prefix-encoder output (HBM-bound;
         # 8 x 43 MB of partials exceed the 256 MB Infinity Cache).
         print("bench: extra lse_merge", file=sys.stderr, flush=True)

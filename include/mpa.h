@@ -211,9 +211,10 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
  *              is MPA_MLA_CALC_SPEC or MPA_MLA_CALC_PREFILL, else NULL (one token
  *              per sequence)
  *   headNum    query heads (1..128 per token; > 0); kvHeadNum must be 1
- *   qkScale, maskType, calcType, cacheMode  see above (the int8 / NZ cache modes
- *              2 and 3 and calcType RING return MPA_ERROR_UNSUPPORTED; RING's
- *              single-GPU part is mpaLseMerge)
+ *   qkScale, maskType, calcType, cacheMode  see above (cacheMode 2 and 3, the
+ *              page's int8 and fp16/bf16 NZ layouts, and calcType RING return
+ *              MPA_ERROR_UNSUPPORTED; the int8 cache is served on the ND layout by
+ *              mpaMLAInt8GetWorkspaceSize, RING's single-GPU part by mpaLseMerge)
  *   batch, numBlocks, blockSize, maxBlockNum, dtype   as for PrefixEncoder
  *   attenOut   dev [T, headNum, 512] dtype (output)
  *   lse        dev [T, headNum] fp32 natural-log LSE (output), or NULL
@@ -226,6 +227,31 @@ mpaStatus mpaMLAGetWorkspaceSize(
     int32_t headNum, float qkScale, int32_t kvHeadNum, int maskType, int calcType,
     int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum,
     int dtype, void *attenOut, float *lse, uint64_t *workspaceSize, mpaOperation **op);
+
+/*
+ * MLA, phase 1, over an int8 latent cache (ATB page "MLA", parameter table:
+ * qNope and ctKV int8, qkDescale and pvDescale [num_heads] float, the
+ * quantised INT8_NZCACHE cache mode) -- on the ND layout instead of the
+ * page's NZ one:
+ *     s_j = qkScale * (qkDescale[h] * (qNope_{t,h} . ctKV_j) + qRope_{t,h} . kRope_j)
+ *     attenOut_{t,h} = pvDescale[h] * sum_j softmax(s)_j ctKV_j,  lse = ln sum_j exp(s_j)
+ * (qNope . ctKV an exact integer dot product over 512 dims; h the query head).
+ *
+ *   qNope      dev [T, headNum, 512] int8      qRope  dev [T, headNum, 64] dtype
+ *   ctKV       dev [numBlocks, blockSize, 1, 512] int8
+ *   kRope      dev [numBlocks, blockSize, 1, 64] dtype (required)
+ *   qkDescale, pvDescale  dev [headNum] fp32 (required)
+ *   dtype      MPA_FP16 or MPA_BF16: the type of qRope, kRope and attenOut
+ * The other arguments, outputs, errors and phase 2 (mpaMLA) are those of
+ * mpaMLAGetWorkspaceSize with cacheMode KROPE_CTKV.
+ */
+mpaStatus mpaMLAInt8GetWorkspaceSize(
+    const void *qNope, const void *qRope, const void *ctKV, const void *kRope,
+    const int32_t *blockTables, const int32_t *contextLens, const int32_t *qSeqLen,
+    const float *qkDescale, const float *pvDescale, int32_t headNum, float qkScale,
+    int32_t kvHeadNum, int maskType, int calcType, int32_t batch, int32_t numBlocks,
+    int32_t blockSize, int32_t maxBlockNum, int dtype, void *attenOut, float *lse,
+    uint64_t *workspaceSize, mpaOperation **op);
 
 /* MLA, phase 2: two launches on `stream` -- split-KV partials into the
  * workspace (>= the size phase 1 returned, 256-byte aligned), then their

@@ -203,16 +203,30 @@ def prefix_encoder(query, key, value, block_tables, seq_len, kv_seq_len, *,
 
 
 class MLA:
-    """A planned MLA decode call (phase 1 of the C ABI); ``run()`` launches it."""
+    """A planned MLA decode call (phase 1 of the C ABI); ``run()`` launches it.
+
+    With int8 ``q_nope`` and ``ct_kv`` (the int8 latent cache) ``qk_descale`` and
+    ``pv_descale`` (float32 [headNum] device tensors) and ``k_rope`` are required;
+    q_rope, k_rope and the output then carry the float16/bfloat16 type."""
 
     def __init__(self, q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, *, qk_scale,
                  q_seq_len=None, mask_type=MLA_MASK_UNDEFINED, calc_type=None, cache_mode=None,
-                 out=None, lse=None, return_lse=False):
+                 out=None, lse=None, return_lse=False, qk_descale=None, pv_descale=None):
         _need(q_nope.is_cuda and q_rope.is_cuda and ct_kv.is_cuda and block_tables.is_cuda,
               "inputs must be device tensors")
-        dt = q_nope.dtype
-        _need(dt in _DTYPES and q_rope.dtype == dt and ct_kv.dtype == dt and
-              (k_rope is None or k_rope.dtype == dt), "inputs must share one dtype, float16 or bfloat16")
+        quant = q_nope.dtype == torch.int8
+        dt = q_rope.dtype
+        if quant:
+            _need(ct_kv.dtype == torch.int8 and k_rope is not None and k_rope.dtype == dt and dt in _DTYPES,
+                  "int8 cache: qNope and ctKV int8, kRope and qRope float16/bfloat16")
+            _need(cache_mode in (None, MLA_CACHE_KROPE_CTKV), "the int8 cache is a separate (ND) cache")
+            for d in (qk_descale, pv_descale):
+                _need(d is not None and d.is_cuda and d.dtype == torch.float32 and d.is_contiguous()
+                      and d.numel() == q_nope.shape[1], "qk_descale / pv_descale: float32 [headNum] on the device")
+        else:
+            _need(qk_descale is None and pv_descale is None, "descales go with the int8 cache only")
+            _need(dt in _DTYPES and q_nope.dtype == dt and ct_kv.dtype == dt and
+                  (k_rope is None or k_rope.dtype == dt), "inputs must share one dtype, float16 or bfloat16")
         _need(q_nope.dim() == 3 and q_nope.shape[2] == 512 and q_rope.shape[:2] == q_nope.shape[:2]
               and q_rope.shape[2] == 64, "qNope [T, H, 512], qRope [T, H, 64]")
         _need(ct_kv.dim() == 4 and ct_kv.shape[2] == 1, "ctKV [numBlocks, blockSize, 1, 512|576]")
@@ -236,7 +250,7 @@ class MLA:
             self._ql, p_ql = _host_i32(q_seq_len)
         else:
             self._ql, p_ql = None, ctypes.POINTER(ctypes.c_int32)()
-        self.out = out if out is not None else torch.empty_like(q_nope)
+        self.out = out if out is not None else torch.empty(q_nope.shape, dtype=dt, device=q_nope.device)
         _need(self.out.shape == q_nope.shape and self.out.dtype == dt and self.out.is_contiguous(),
               "out must be [T, H, 512] of the input dtype")
         if lse is None and return_lse:
@@ -245,16 +259,24 @@ class MLA:
             _need(lse.dtype == torch.float32 and tuple(lse.shape) == (T, H) and lse.is_contiguous(),
                   "lse must be float32 [T, headNum]")
         self.lse = lse
-        self._keep = (q_nope, q_rope, ct_kv, k_rope, block_tables)
+        self._keep = (q_nope, q_rope, ct_kv, k_rope, block_tables, qk_descale, pv_descale)
         self.device = q_nope.device
         ws = ctypes.c_uint64(0)
         op = ctypes.c_void_p(0)
-        st = LIB.mpaMLAGetWorkspaceSize(
-            _ptr(q_nope), _ptr(q_rope), _ptr(ct_kv), _ptr(k_rope), _ptr(block_tables), p_ctx, p_ql,
-            H, float(qk_scale), 1, int(mask_type), int(calc_type), int(cache_mode), B,
-            ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], _ptr(self.out),
-            _ptr(lse), ctypes.byref(ws), ctypes.byref(op))
-        _check(st, "mpaMLAGetWorkspaceSize")
+        if quant:
+            st = LIB.mpaMLAInt8GetWorkspaceSize(
+                _ptr(q_nope), _ptr(q_rope), _ptr(ct_kv), _ptr(k_rope), _ptr(block_tables), p_ctx, p_ql,
+                _ptr(qk_descale), _ptr(pv_descale), H, float(qk_scale), 1, int(mask_type), int(calc_type),
+                B, ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], _ptr(self.out),
+                _ptr(lse), ctypes.byref(ws), ctypes.byref(op))
+            _check(st, "mpaMLAInt8GetWorkspaceSize")
+        else:
+            st = LIB.mpaMLAGetWorkspaceSize(
+                _ptr(q_nope), _ptr(q_rope), _ptr(ct_kv), _ptr(k_rope), _ptr(block_tables), p_ctx, p_ql,
+                H, float(qk_scale), 1, int(mask_type), int(calc_type), int(cache_mode), B,
+                ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], _ptr(self.out),
+                _ptr(lse), ctypes.byref(ws), ctypes.byref(op))
+            _check(st, "mpaMLAGetWorkspaceSize")
         self._op = op
         self.workspace = (torch.empty(ws.value, dtype=torch.uint8, device=q_nope.device)
                           if ws.value else None)
@@ -280,11 +302,11 @@ class MLA:
 
 def mla(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, *, qk_scale, q_seq_len=None,
         mask_type=MLA_MASK_UNDEFINED, calc_type=None, cache_mode=None, out=None, lse=None,
-        return_lse=False, stream=None):
+        return_lse=False, stream=None, qk_descale=None, pv_descale=None):
     """One MLA decode call; returns out, or (out, lse) with return_lse."""
     op = MLA(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, qk_scale=qk_scale,
              q_seq_len=q_seq_len, mask_type=mask_type, calc_type=calc_type, cache_mode=cache_mode,
-             out=out, lse=lse, return_lse=return_lse)
+             out=out, lse=lse, return_lse=return_lse, qk_descale=qk_descale, pv_descale=pv_descale)
     try:
         return op.run(stream)
     finally:

@@ -46,6 +46,13 @@ SIGNATURES = {
         ctypes.c_int, ctypes.c_int, ctypes.c_int,    # maskType, calcType, cacheMode
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, numBlocks, blockSize, maxBlockNum
         ctypes.c_int, c_vp, c_vp, c_u64p, c_opp]),   # dtype, attenOut, lse, workspaceSize, op
+    "mpaMLAInt8GetWorkspaceSize": (ctypes.c_int32, [
+        c_vp, c_vp, c_vp, c_vp, c_vp,                # qNope, qRope, ctKV, kRope, blockTables
+        c_i32p, c_i32p, c_vp, c_vp,                  # contextLens, qSeqLen, qkDescale, pvDescale
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32,  # headNum, qkScale, kvHeadNum
+        ctypes.c_int, ctypes.c_int,                  # maskType, calcType
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, numBlocks, blockSize, maxBlockNum
+        ctypes.c_int, c_vp, c_vp, c_u64p, c_opp]),   # dtype, attenOut, lse, workspaceSize, op
     "mpaMLA": (ctypes.c_int32, [c_vp, ctypes.c_uint64, c_vp, c_vp]),
     "mpaLseMerge": (ctypes.c_int32, [
         c_vp, c_vp, ctypes.c_int32, ctypes.c_int64,  # oParts, lseParts, nParts, rows

@@ -335,15 +335,17 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize,
   return MPA_OK;
 }
 
-mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const void* ctKV,
-                                 const void* kRope, const int32_t* blockTables,
-                                 const int32_t* contextLens, const int32_t* qSeqLen, int32_t headNum,
-                                 float qkScale, int32_t kvHeadNum, int maskType, int calcType,
-                                 int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
-                                 int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
-                                 uint64_t* workspaceSize, mpaOperation** op) {
-  g_last_error.clear();
-  if (op) *op = nullptr;
+namespace {
+
+// Phase 1 of MLA after the entry point's own checks; quant selects the int8
+// latent cache (qNope / ctKV int8, separate kRope, per-head descales).
+mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, const void* kRope,
+                      const int32_t* blockTables, const int32_t* contextLens, const int32_t* qSeqLen,
+                      int32_t headNum, float qkScale, int32_t kvHeadNum, int maskType, int calcType,
+                      int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
+                      int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
+                      uint64_t* workspaceSize, mpaOperation** op, bool quant, const float* qkDescale,
+                      const float* pvDescale) {
   if (!op || !workspaceSize) return fail(MPA_ERROR_INVALID_ARG, "workspaceSize and op must not be NULL");
   if (!qNope || !qRope || !ctKV || !blockTables || !attenOut)
     return fail(MPA_ERROR_INVALID_ARG, "qNope, qRope, ctKV, blockTables and attenOut are required");
@@ -352,8 +354,13 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   if (headNum <= 0) return fail(MPA_ERROR_INVALID_ARG, "headNum must be > 0");
   if (kvHeadNum != 1) return fail(MPA_ERROR_UNSUPPORTED, "MLA supports kvHeadNum == 1 only (got %d)", kvHeadNum);
   if (dtype != MPA_FP16 && dtype != MPA_BF16) return fail(MPA_ERROR_INVALID_ARG, "dtype must be fp16 or bf16");
+  if (quant && (!qkDescale || !pvDescale))
+    return fail(MPA_ERROR_INVALID_ARG, "the int8 cache needs qkDescale and pvDescale");
   if (cacheMode != MPA_MLA_CACHE_KVCACHE && cacheMode != MPA_MLA_CACHE_KROPE_CTKV)
-    return fail(MPA_ERROR_UNSUPPORTED, "cacheMode %d is not supported (0, 1)", cacheMode);
+    return fail(MPA_ERROR_UNSUPPORTED,
+                "cacheMode %d is not supported (0, 1; the int8 cache has its own entry point, "
+                "mpaMLAInt8GetWorkspaceSize, on the ND layout)",
+                cacheMode);
   if (cacheMode == MPA_MLA_CACHE_KROPE_CTKV && !kRope)
     return fail(MPA_ERROR_INVALID_ARG, "cacheMode 1 needs kRope");
   if (cacheMode == MPA_MLA_CACHE_KVCACHE && kRope)
@@ -442,12 +449,47 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
   p.max_rows = plan.max_rows;
   p.any_parts = any_parts ? 1 : 0;
   p.scale2 = qkScale * kLog2e;
+  p.quant = quant ? 1 : 0;
+  p.qk_descale = qkDescale;
+  p.pv_descale = pvDescale;
   o->part_o_off = 0;
   o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 2 + 255) & ~uint64_t(255);
   o->ws_bytes = o->part_lse_off + (((uint64_t)plan.part_rows * 4 + 255) & ~uint64_t(255));
   *workspaceSize = o->ws_bytes;
   *op = o;
   return MPA_OK;
+}
+
+}  // namespace
+
+mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const void* ctKV,
+                                 const void* kRope, const int32_t* blockTables,
+                                 const int32_t* contextLens, const int32_t* qSeqLen, int32_t headNum,
+                                 float qkScale, int32_t kvHeadNum, int maskType, int calcType,
+                                 int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
+                                 int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
+                                 uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  return make_mla_op(qNope, qRope, ctKV, kRope, blockTables, contextLens, qSeqLen, headNum, qkScale,
+                     kvHeadNum, maskType, calcType, cacheMode, batch, numBlocks, blockSize, maxBlockNum,
+                     dtype, attenOut, lse, workspaceSize, op, false, nullptr, nullptr);
+}
+
+mpaStatus mpaMLAInt8GetWorkspaceSize(const void* qNope, const void* qRope, const void* ctKV,
+                                     const void* kRope, const int32_t* blockTables,
+                                     const int32_t* contextLens, const int32_t* qSeqLen,
+                                     const float* qkDescale, const float* pvDescale, int32_t headNum,
+                                     float qkScale, int32_t kvHeadNum, int maskType, int calcType,
+                                     int32_t batch, int32_t numBlocks, int32_t blockSize,
+                                     int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
+                                     uint64_t* workspaceSize, mpaOperation** op) {
+  g_last_error.clear();
+  if (op) *op = nullptr;
+  if (!kRope) return fail(MPA_ERROR_INVALID_ARG, "the int8 cache keeps the rope part in kRope: it is required");
+  return make_mla_op(qNope, qRope, ctKV, kRope, blockTables, contextLens, qSeqLen, headNum, qkScale,
+                     kvHeadNum, maskType, calcType, MPA_MLA_CACHE_KROPE_CTKV, batch, numBlocks, blockSize,
+                     maxBlockNum, dtype, attenOut, lse, workspaceSize, op, true, qkDescale, pvDescale);
 }
 
 mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void* stream) {

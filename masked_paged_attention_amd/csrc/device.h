@@ -15,6 +15,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Vec;
@@ -37,6 +41,21 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, int32) += A(32x32) * B(32x32), int8 operands.  Lane l supplies A row
+// l%32 and B column l%32, each with the 16 contraction indices 16*(l/32) ..
+// +15; D in the layout of mfma32 (checked on gfx950).
+__device__ __forceinline__ i32x16 mfma32_i8(i32x4 a, i32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of 8-bit data.  In each group of 16 lanes, source lane s
+// points at 8 consecutive bytes (row s/2, bytes 8*(s%2)..+7 of an 8 x 16 block;
+// the rows may lie anywhere); lane i of the group receives byte column i of
+// the 8 rows, row e in byte e (checked on gfx950).
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3)))*)p);
 }
 
 // LDS transpose read of 16-bit data.  In each group of 16 lanes, source lane s

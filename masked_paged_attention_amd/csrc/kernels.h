@@ -66,6 +66,9 @@ struct MlaParams {
   int max_rows;                // largest q_len * H (combine grid)
   int any_parts;               // some sequence has partial results to merge
   float scale2;                // qkScale * log2(e)
+  int quant;                   // 1: int8 qNope / ctKV with per-head descales
+  const float* qk_descale;     // [H] (quant only)
+  const float* pv_descale;     // [H] (quant only)
 };
 
 hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream);

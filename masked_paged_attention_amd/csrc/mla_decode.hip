@@ -68,18 +68,49 @@ __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 // chunks, odd), read 32 rows at a time as the B operand.
 constexpr int kQRopeRow = 72;
 
-template <typename T, bool ONE_BLOCK>
+// int8 latent cache: slot s (key lat_slot(s)) holds the key's 512 bytes at
+// byte 1040 (s % 16) + 512 (s / 16): slots s and s + 16 are adjacent, so one
+// direct load (lanes 0..31 and 32..63) fills both, and the 16-byte padding per
+// pair puts slot s at bank group s % 16 (+ column) for both read patterns --
+// the QK operand (16 slots, one 16-byte column) and the 8-bit transpose read
+// (8 slots, 16 bytes each).
+constexpr int kQ8PairBytes = 2 * kDv + 16;
+constexpr int kQ8LatBytes = 16 * kQ8PairBytes;
+__device__ __forceinline__ int q8_slot_byte(int s) { return kQ8PairBytes * (s & 15) + kDv * (s >> 4); }
+
+// 8 signed bytes -> 8 fp16 values, exact: byte x ^ 0x80 = x + 128 placed under
+// the fp16 exponent byte 0x64 is the value 1024 + (x + 128); subtracting 1152
+// leaves x.
+__device__ __forceinline__ f16x8 i8x8_to_f16x8(i32x2 t) {
+  const unsigned a = (unsigned)t[0] ^ 0x80808080u;
+  const unsigned b = (unsigned)t[1] ^ 0x80808080u;
+  u32x4 w;
+  w[0] = (a & 0xFFu) | ((a & 0xFF00u) << 8) | 0x64006400u;
+  w[1] = ((a >> 16) & 0xFFu) | ((a >> 8) & 0xFF0000u) | 0x64006400u;
+  w[2] = (b & 0xFFu) | ((b & 0xFF00u) << 8) | 0x64006400u;
+  w[3] = ((b >> 16) & 0xFFu) | ((b >> 8) & 0xFF0000u) | 0x64006400u;
+  const _Float16 k = (_Float16)1152.0f;
+  return __builtin_bit_cast(f16x8, w) - (f16x8){k, k, k, k, k, k, k, k};
+}
+
+// Q8: the int8 latent cache (qNope and ctKV int8, per-head descales) -- the
+// nope part of the scores on the int8 MFMA (exact integer products), the value
+// side through the 8-bit transpose read and an exact fp16 conversion.
+template <typename T, bool ONE_BLOCK, bool Q8>
 __global__ void __launch_bounds__(512, 1)
     mla_split_kernel(MlaParams p, const int32_t* __restrict__ block_tables,
                      const int4* __restrict__ segs, const int32_t* __restrict__ piece_seg,
                      const int4* __restrict__ seqs, const int4* __restrict__ seqs2) {
   using V8 = typename Vec<T>::x8;
+  using PV8 = std::conditional_t<Q8, f16x8, V8>;  // operands of O^T += V^T P^T
+  using PT = std::conditional_t<Q8, _Float16, T>;
   constexpr int NCH = kDv / 16 / 2;  // 16 register-resident contraction chunks per wave of a pair
+  constexpr int NCH8 = kDv / 32 / 2; // 8 int8 chunks (32 dims) per wave of a pair
   constexpr int NDT = kDv / 32 / 2;  // 8 O^T tiles per wave of a pair
 
   // Three key-tile buffers (latent rows, then rope rows), the pairs' partial
   // S^T exchange, and the rope part of the 128 query rows.
-  constexpr int kLatElems = kBN * kLatRow;
+  constexpr int kLatElems = Q8 ? kQ8LatBytes / (int)sizeof(T) : kBN * kLatRow;
   constexpr int kBufElems = kLatElems + kBN * 64;
   __shared__ __attribute__((aligned(1024))) T tbuf[3 * kBufElems];
   __shared__ __attribute__((aligned(16))) float4 xch[kWaves][4 * 64];
@@ -155,6 +186,42 @@ __global__ void __launch_bounds__(512, 1)
   auto issue = [&](int blk, T* buf) __attribute__((always_inline)) {
     const int last = lk1 - 1 - lj;  // last key of the segment within the tile
     const unsigned m0buf = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)buf;
+    if constexpr (Q8) {
+      // Latent: wave w fills slots 4w .. 4w+3 and the same + 16 (lanes 32..63),
+      // 32 lanes x 16 bytes per key; rope as below.
+      const int ln = opaque_lane();
+      const int half = ln >> 5;
+      const unsigned col = 16u * (unsigned)(ln & 31);
+      const int ropekey = 8 * w + (ln >> 3);
+      const unsigned ropecol = 16u * (unsigned)((ln & 7) ^ rope_swz(ropekey));
+      if constexpr (ONE_BLOCK) {
+        const long long rt = (long long)blk * p.block_size + (lj & (p.block_size - 1));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int key = min(lat_slot(4 * w + k) + 16 * half, last);
+          dma16s_m0((const char*)p.ckv + rt * kDv, (unsigned)key * kDv + col,
+                    m0buf + (unsigned)q8_slot_byte(4 * w + k));
+        }
+        dma16s((const char*)p.krope + rt * 64 * (long long)sizeof(T),
+               (unsigned)min(ropekey, last) * 64u * (unsigned)sizeof(T) + ropecol,
+               buf + kLatElems + 64 * 8 * w);
+      } else {
+        const int32_t* bt = block_tables + (long long)lb * p.max_blocks;
+        auto row_of = [&](int key) -> long long {
+          const int j = lj + min(key, last);
+          const int bi = j / p.block_size;
+          return (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
+        };
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const long long row = row_of(lat_slot(4 * w + k) + 16 * half);
+          dma16((const char*)p.ckv + row * kDv + col, (const char*)buf + q8_slot_byte(4 * w + k));
+        }
+        dma16((const char*)p.krope + row_of(ropekey) * 64 * (long long)sizeof(T) + ropecol,
+              buf + kLatElems + 64 * 8 * w);
+      }
+      return;
+    }
     if constexpr (ONE_BLOCK) {
       // The tile lies in one cache block: its keys are consecutive rows.
       const long long rt = (long long)blk * p.block_size + (lj & (p.block_size - 1));
@@ -189,18 +256,20 @@ __global__ void __launch_bounds__(512, 1)
             buf + kLatElems + 64 * 8 * w);
     }
   };
-  // Waves 0..3 issue 9 direct loads per tile, so "s_waitcnt vmcnt(9)" waits for
-  // every tile but the most recently issued one.  (Encoding: vmcnt | expcnt 7
+  // Waves 0..3 issue 9 direct loads per tile (5 with the int8 cache), so
+  // "s_waitcnt vmcnt(9)" waits for every tile but the most recently issued one.  (Encoding: vmcnt | expcnt 7
   // << 4 | lgkmcnt 15 << 8, i.e. wait on vector memory only; through the
   // builtin so that the compiler's own wait tracking sees it.)  A loader wave
   // waits for its own loads; the barrier after it publishes the tile to all.
   auto wait_tiles = [&](bool newer_in_flight) __attribute__((always_inline)) {
-    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | 9);
+    if (newer_in_flight) __builtin_amdgcn_s_waitcnt(0xF70 | (Q8 ? 5 : 9));  // Q8: 4 latent + 1 rope
     else __builtin_amdgcn_s_waitcnt(0xF70);
   };
 
   // ---- per-segment state ----
-  V8 qreg[NCH];
+  V8 qreg[Q8 ? 1 : NCH];
+  i32x4 qreg8[Q8 ? NCH8 : 1];
+  float qk_desc = 1.0f, pv_desc = 1.0f, pv_desc_next = 1.0f;  // Q8: this lane's row's head
   f32x16 o[NDT];
   float m_run = -INFINITY, l_run = 0.0f;
   bool row_ok = false, w_active = false;
@@ -225,14 +294,26 @@ __global__ void __launch_bounds__(512, 1)
     const int ln = opaque_lane();
     const int mm_row = row_base + 32 * pr + (ln & 31);
     const bool ok = mm_row < rows;
-    const T* qn = (const T*)p.q_nope + ((long long)tok0 * H + (ok ? mm_row : 0)) * kDv + 8 * (ln >> 5);
+    if constexpr (Q8) {
+      // int8 nope: lane (row, g) holds dims 256hf + 32c + 16g .. +15 of chunk c;
+      // the descales of the row's head (rows are (token, head) pairs).
+      const int8_t* qn8 = (const int8_t*)p.q_nope + ((long long)tok0 * H + (ok ? mm_row : 0)) * kDv +
+                          256 * hf + 16 * (ln >> 5);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (ok) {
-        qreg[c] = *(const V8*)(qn + 16 * (NCH * hf + c));
-      } else {
+      for (int c = 0; c < NCH8; ++c) qreg8[c] = ok ? *(const i32x4*)(qn8 + 32 * c) : i32x4{0, 0, 0, 0};
+      const int hd = ok ? mm_row % H : 0;
+      qk_desc = p.qk_descale[hd];
+      pv_desc_next = p.pv_descale[hd];
+    } else {
+      const T* qn = (const T*)p.q_nope + ((long long)tok0 * H + (ok ? mm_row : 0)) * kDv + 8 * (ln >> 5);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
+      for (int c = 0; c < NCH; ++c) {
+        if (ok) {
+          qreg[c] = *(const V8*)(qn + 16 * (NCH * hf + c));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qreg[c][e] = (T)0.0f;
+        }
       }
     }
 #pragma unroll
@@ -271,11 +352,50 @@ __global__ void __launch_bounds__(512, 1)
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     m_run = -INFINITY;
     l_run = 0.0f;
+    pv_desc = pv_desc_next;
   };
 
   // First half of a tile: the wave's partial S^T over its half of the 576
   // dims, written to its exchange slot.
   auto qk_part = [&](const T* lat) __attribute__((always_inline)) {
+    if constexpr (Q8) {
+      if (!w_active) return;
+      // Nope: int8 A operands (key slot lat_slot(lq), dims 256hf + 32c + 16g ..
+      // +15), loaded two chunks ahead; exact int32 sums, then the head's descale;
+      // the rope MFMAs accumulate on top.
+      const char* arow = (const char*)lat + q8_slot_byte(lat_slot(lq)) + 256 * hf + 16 * g;
+      i32x4 ring[2];
+      ring[0] = *(const i32x4*)(arow);
+      ring[1] = *(const i32x4*)(arow + 32);
+      i32x16 si = i32x16{};
+      V8 ra0, ra1, bq0, bq1;
+#pragma unroll
+      for (int c = 0; c < NCH8; ++c) {
+        const i32x4 a = ring[c & 1];
+        if (c + 2 < NCH8) ring[c & 1] = *(const i32x4*)(arow + 32 * (c + 2));
+        if (c == NCH8 - 3) {
+          const int ln = opaque_lane();
+          const int key = ln & 31;
+          const int r0 = 2 * (2 * hf) + (ln >> 5);
+          ra0 = *(const V8*)(lat + kLatElems + key * 64 + 8 * (r0 ^ rope_swz(key)));
+          ra1 = *(const V8*)(lat + kLatElems + key * 64 + 8 * ((r0 + 2) ^ rope_swz(key)));
+          const T* qrow = qrope + (32 * pr + lq) * kQRopeRow + 8 * g;
+          bq0 = *(const V8*)(qrow + 8 * (4 * hf));
+          bq1 = *(const V8*)(qrow + 8 * (4 * hf + 2));
+        }
+        si = mfma32_i8(a, qreg8[c], si);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f32x16 s0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = (float)si[r] * qk_desc;
+      s0 = mfma32(ra0, bq0, s0);
+      s0 = mfma32(ra1, bq1, s0);
+#pragma unroll
+      for (int r = 0; r < 16; r += 4)
+        my_x[16 * r] = make_float4(s0[r], s0[r + 1], s0[r + 2], s0[r + 3]);
+      return;
+    }
     f32x16 s0 = f32x16{};
     // A operands: this lane's key row (slot), 16-byte chunks of this wave's half
     // of the contraction: 16 latent chunks, then 2 rope chunks.  Loads run
@@ -325,12 +445,23 @@ __global__ void __launch_bounds__(512, 1)
       // V^T operands (keys 16kc + tr_row and the same + 8, i.e. slot + 2; dims
       // 32dt + tr_col .. +3), loaded kPvDepth MFMAs ahead; the first ones are in
       // flight during the softmax.
+      // Q8: lane (group of 16, index s) points at key 4g + (e & 3) + 8 (e >> 2),
+      // e = s / 2 (the key order of the P^T operand; key half i >> 3 is 512
+      // bytes on), bytes 8 (s % 2) .. +7 of the group's 16 dims; the transpose
+      // read returns this lane's dim over those 8 keys.
+      const int e8 = (l & 15) >> 1;
+      const char* vbase8 = (const char*)lat + q8_slot_byte(lat_slot(4 * g + (e8 & 3) + 8 * (e8 >> 2))) +
+                           256 * hf + 16 * ((l >> 4) & 1) + 8 * (l & 1);
       const T* vbase = lat + lat_slot(tr_row) * kLatRow + tr_col;
-      auto load_v = [&](int i) -> V8 {
-        const T* src0 = vbase + (i >> 3) * (16 * kLatRow) + 32 * (i & 7);
-        const s16x4 lo = lds_read_tr16(src0);
-        const s16x4 hi = lds_read_tr16(src0 + 2 * kLatRow);
-        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      auto load_v = [&](int i) -> PV8 {
+        if constexpr (Q8) {
+          return i8x8_to_f16x8(lds_read_tr8(vbase8 + kDv * (i >> 3) + 32 * (i & 7)));
+        } else {
+          const T* src0 = vbase + (i >> 3) * (16 * kLatRow) + 32 * (i & 7);
+          const s16x4 lo = lds_read_tr16(src0);
+          const s16x4 hi = lds_read_tr16(src0 + 2 * kLatRow);
+          return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       };
       constexpr int kPvDepth = 2;
 #pragma unroll
@@ -339,7 +470,7 @@ __global__ void __launch_bounds__(512, 1)
         const float4 v = other_x[16 * r];
         s0[r] = u.x + v.x; s0[r + 1] = u.y + v.y; s0[r + 2] = u.z + v.z; s0[r + 3] = u.w + v.w;
       }
-      V8 vring[kPvDepth];
+      PV8 vring[kPvDepth];
 #pragma unroll
       for (int c = 0; c < kPvDepth; ++c) vring[c] = load_v(c);
       // Row max of the scaled scores; the exponent below is fma(s, kmul, -m):
@@ -389,15 +520,15 @@ __global__ void __launch_bounds__(512, 1)
         psum += s0[r];
       }
       l_run += psum;
-      V8 p0, p1;
+      PV8 p0, p1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p0[e] = (T)s0[e];
-        p1[e] = (T)s0[8 + e];
+        p0[e] = (PT)s0[e];
+        p1[e] = (PT)s0[8 + e];
       }
 #pragma unroll
       for (int i = 0; i < 2 * NDT; ++i) {
-        const V8 a = vring[i % kPvDepth];
+        const PV8 a = vring[i % kPvDepth];
         if (i + kPvDepth < 2 * NDT) vring[i % kPvDepth] = load_v(i + kPvDepth);
         o[i & 7] = mfma32(a, (i >> 3) == 0 ? p0 : p1, o[i & 7]);
       }
@@ -417,7 +548,7 @@ __global__ void __launch_bounds__(512, 1)
     const int ln = opaque_lane();
     const int mr = row_base + 32 * pr + (ln & 31);
     const int gl = ln >> 5;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (Q8 ? pv_desc : 1.0f);
     const float lse2 = l_tot > 0.0f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
     T* orow;
     if (sg.w < 0) {
@@ -568,14 +699,22 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
   }
 }
 
-template <typename T>
-hipError_t launch_typed(const MlaParams& p, hipStream_t s) {
+template <typename T, bool Q8>
+void launch_split(const MlaParams& p, hipStream_t s) {
   if (p.bs_shift >= 5)
-    hipLaunchKernelGGL((mla_split_kernel<T, true>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
+    hipLaunchKernelGGL((mla_split_kernel<T, true, Q8>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
                        p.segs, p.piece_seg, p.seqs, p.seqs2);
   else
-    hipLaunchKernelGGL((mla_split_kernel<T, false>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
+    hipLaunchKernelGGL((mla_split_kernel<T, false, Q8>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
                        p.segs, p.piece_seg, p.seqs, p.seqs2);
+}
+
+template <typename T>
+hipError_t launch_typed(const MlaParams& p, hipStream_t s) {
+  if (p.quant)
+    launch_split<T, true>(p, s);
+  else
+    launch_split<T, false>(p, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.any_parts) return e;
   hipLaunchKernelGGL(mla_combine_kernel<T>, dim3((p.max_rows + 3) / 4, p.batch), dim3(256), 0, s, p,

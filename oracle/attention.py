@@ -228,8 +228,18 @@ def _mla_qlens(batch, q_seq_len, calc_type):
 
 
 def mla_rows(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, q_seq_len,
-             head_num, qk_scale, mask_type, calc_type, rows):
-    """MLA oracle for selected (token, head) pairs.  Returns (O [n,512], LSE [n])."""
+             head_num, qk_scale, mask_type, calc_type, rows, qk_descale=None, pv_descale=None):
+    """MLA oracle for selected (token, head) pairs.  Returns (O [n,512], LSE [n]).
+
+    With ``qk_descale`` / ``pv_descale`` ([headNum]) the cache is the int8 one of
+    the MLA page's parameter table (qNope and ctKV int8, rows qkDescale and
+    pvDescale): for head h the nope part of the score is qkDescale[h] times the
+    integer dot product qNope . ctKV, the rope part stays as it is, and the output
+    is pvDescale[h] times the softmax-weighted ctKV rows.
+    """
+    quant = qk_descale is not None
+    if quant != (pv_descale is not None):
+        raise ValueError("qk_descale and pv_descale go together")
     batch = len(context_lens)
     qlens = _mla_qlens(batch, q_seq_len, calc_type)
     block_size = ct_kv.shape[1]
@@ -259,9 +269,10 @@ def mla_rows(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, q_seq_le
             k = np.concatenate([lat, _gather(k_rope, block_tables, b, ctx, block_size, 0)], axis=1)
             v = lat
         idx = np.array([it[0] for it in items])
-        qs = np.stack([np.concatenate([np.asarray(q_nope[tok, h], dtype=np.float64),
+        qk_d = [float(np.float32(qk_descale[h])) if quant else 1.0 for _, _, h in items]
+        qs = np.stack([np.concatenate([np.asarray(q_nope[tok, h], dtype=np.float64) * qd,
                                        np.asarray(q_rope[tok, h], dtype=np.float64)])
-                       for _, tok, h in items])
+                       for (_, tok, h), qd in zip(items, qk_d)])
         t = np.array([tok_t[tok] for _, tok, _ in items])
         j = np.arange(ctx)[None, :]
         if mask_type == MLA_MASK_SPEC:
@@ -271,17 +282,21 @@ def mla_rows(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, q_seq_le
         else:
             raise ValueError(f"unsupported MLA maskType {mask_type}")
         msk = np.where(vis, 0.0, -np.inf)
-        o, ls = attend(qs, k, v, scale, msk)
+        o, ls = attend(qs, np.asarray(k, dtype=np.float64), np.asarray(v, dtype=np.float64), scale, msk)
+        if quant:
+            o = o * np.array([float(np.float32(pv_descale[h])) for _, _, h in items])[:, None]
         out[idx] = o
         lse[idx] = ls
     return out, lse
 
 
 def mla(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens, q_seq_len,
-        head_num, qk_scale, mask_type=MLA_MASK_UNDEFINED, calc_type=MLA_CALC_UNDEFINED):
+        head_num, qk_scale, mask_type=MLA_MASK_UNDEFINED, calc_type=MLA_CALC_UNDEFINED,
+        qk_descale=None, pv_descale=None):
     """Full MLA oracle: (O [T, headNum, 512] fp64, LSE [T, headNum] fp64)."""
     n_tok = q_nope.shape[0]
     rows = [(t, h) for t in range(n_tok) for h in range(head_num)]
     o, ls = mla_rows(q_nope, q_rope, ct_kv, k_rope, block_tables, context_lens,
-                     q_seq_len, head_num, qk_scale, mask_type, calc_type, rows)
+                     q_seq_len, head_num, qk_scale, mask_type, calc_type, rows,
+                     qk_descale, pv_descale)
     return o.reshape(n_tok, head_num, -1), ls.reshape(n_tok, head_num)

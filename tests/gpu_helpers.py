@@ -97,13 +97,18 @@ def check_prefill_sampled(case, out, lse, n=192, seed=0):
 def gpu_mla(case, return_lse=True):
     import masked_paged_attention_amd as mpa
     lse = None
-    out = torch.empty_like(case.q_nope)
+    out = torch.empty((case.n_tokens, case.head_num, 512), dtype=case.q_rope.dtype, device=case.q_rope.device)
     if return_lse:
         lse = torch.full((case.n_tokens, case.head_num), float("nan"), dtype=torch.float32,
                          device=case.q_nope.device)
+    qkd = pvd = None
+    if case.qk_descale is not None:
+        qkd = torch.as_tensor(case.qk_descale, device=case.q_nope.device)
+        pvd = torch.as_tensor(case.pv_descale, device=case.q_nope.device)
     mpa.mla(case.q_nope, case.q_rope, case.ct_kv, case.k_rope, case.block_tables, case.context_lens,
             qk_scale=case.qk_scale, q_seq_len=case.q_seq_len, mask_type=case.mask_type,
-            calc_type=case.calc_type, cache_mode=case.cache_mode, out=out, lse=lse)
+            calc_type=case.calc_type, cache_mode=case.cache_mode, out=out, lse=lse,
+            qk_descale=qkd, pv_descale=pvd)
     torch.cuda.synchronize()
     return out, lse
 

@@ -328,3 +328,32 @@ def test_compressed_mask_valid_args_reach_hip_or_succeed(lib):
         assert st in (0, 4), lib.mpaGetLastErrorMessage()
         if st == 0:
             assert lib.mpaDestroyOperation(op) == 0
+
+
+def _mla8(lib, qkd=FAKE, pvd=FAKE, kr=FAKE, KVH=1, calc=0, ql=None, dtype=1):
+    ctx, pc = _i32([100, 300])
+    pq = _i32(ql)[1] if ql is not None else ctypes.POINTER(ctypes.c_int32)()
+    ws = ctypes.c_uint64(0)
+    op = ctypes.c_void_p(0xdead)
+    st = lib.mpaMLAInt8GetWorkspaceSize(FAKE, FAKE, FAKE, kr, FAKE, pc, pq, qkd, pvd, 16, 0.07, KVH,
+                                        0, calc, 2, 8, 64, 5, dtype, FAKE, None,
+                                        ctypes.byref(ws), ctypes.byref(op))
+    return st, op
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkd=None), 1), (dict(pvd=None), 1), (dict(kr=None), 1), (dict(KVH=2), 2),
+    (dict(calc=1), 1),                   # SPEC without qSeqLen
+    (dict(dtype=2), 1),
+])
+def test_mla_int8_validation(lib, kw, status):
+    st, op = _mla8(lib, **kw)
+    assert st == status, lib.mpaGetLastErrorMessage()
+    assert op.value is None or op.value == 0
+
+
+def test_mla_int8_valid_args_reach_hip_or_succeed(lib):
+    st, op = _mla8(lib)
+    assert st in (0, 4), lib.mpaGetLastErrorMessage()
+    if st == 0:
+        assert lib.mpaDestroyOperation(op) == 0

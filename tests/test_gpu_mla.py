@@ -106,3 +106,67 @@ def test_prefill_128_heads_sampled():
     rows = sorted({(int(rng.integers(T)), int(rng.integers(H))) for _ in range(160)} |
                   {(0, 0), (T - 1, H - 1), (255, 5), (256, 7)})
     check_mla(c, out, lse, rows=rows)
+
+
+# ---- int8 latent cache (qNope / ctKV int8, per-head qkDescale / pvDescale) ----
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_int8_small_decode(dtype):
+    log(f"case mla int8 small q_len 1 dtype={dtype}")
+    c = W.make_mla_int8(81, [100, 37, 300, 1], None, 16, 64, dtype, 0, 0, 0.07, poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse)
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_int8_spec_128_heads(mask):
+    log(f"case mla int8 spec q_len [4, 2, 3] H 128 mask={mask}")
+    c = W.make_mla_int8(83, [70, 500, 1029], [4, 2, 3], 128, 128, "bf16", mask, 1, 1 / np.sqrt(192),
+                        poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse)
+
+
+def test_int8_odd_block_size_and_heads():
+    # blockSize 24: every key looks its block up (no one-block tiles)
+    log("case mla int8 blockSize 24, 20 heads, q_len 3")
+    c = W.make_mla_int8(85, [95, 48, 3], [3, 3, 3], 20, 24, "fp16", 1, 1, 0.05, poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse)
+
+
+def test_int8_mixed_lengths_cross_pieces():
+    log("case mla int8 mixed lengths 128 heads")
+    ctx = [5000, 33, 1, 4096, 127, 7777, 64, 2500]
+    c = W.make_mla_int8(87, ctx, None, 128, 128, "bf16", 0, 0, 1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(6)
+    rows = sorted({(int(rng.integers(len(ctx))), int(rng.integers(128))) for _ in range(200)} |
+                  {(b, h) for b in range(len(ctx)) for h in (0, 127)})
+    check_mla(c, out, lse, rows=rows)
+
+
+def test_int8_full_size_sampled():
+    # the decode workload's shape (64 sequences, contextLens U{1024..8192}, 128 heads)
+    log("case mla int8 full-size decode (sampled rows)")
+    rng = np.random.default_rng(1001)
+    ctx = rng.integers(1024, 8192, size=64, endpoint=True)
+    c = W.make_mla_int8(89, ctx, None, 128, 128, "bf16", 0, 0, 1 / np.sqrt(192), poison=True,
+                        max_block_num=64).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(7)
+    T, H = c.n_tokens, c.head_num
+    rows = sorted({(int(rng.integers(T)), int(rng.integers(H))) for _ in range(160)} |
+                  {(0, 0), (T - 1, H - 1)})
+    check_mla(c, out, lse, rows=rows)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_int8_prefill_and_determinism():
+    log("case mla int8 prefill q_len [40, 64, 9] H 16 causal, run twice")
+    c = W.make_mla_int8(91, [40, 700, 300], [40, 64, 9], 16, 128, "bf16", 1, 3, 1 / np.sqrt(192),
+                        poison=True).to(DEV)
+    o1, l1 = gpu_mla(c)
+    check_mla(c, o1, l1)
+    o2, l2 = gpu_mla(c)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -596,3 +596,67 @@ def test_chunked_mask_special_cases():
         row += L[b]
     with pytest.raises(ValueError):
         oracle.prefix_encoder(query, key, value, bt, L, kv, None, M.MASK_CHUNKED_CAUSAL, 2, 2, 0.7)
+
+
+def _brute_mla_int8(qn, qr, ckv, kr, bt, ctx, qlens, H, scale, qkd, pvd, spec):
+    """Pure-Python int8 MLA (MLA page, parameter table: int8 qNope / ctKV with
+    per-head qkDescale / pvDescale): exact integer nope dot products, descales
+    applied to the score and the output, softmax with math.exp."""
+    bs = ckv.shape[1]
+    out, lse = [], []
+    tok = 0
+    for b in range(len(ctx)):
+        rows = [(int(bt[b][j // bs]), j % bs) for j in range(int(ctx[b]))]
+        for t in range(int(qlens[b])):
+            for h in range(H):
+                lim = int(ctx[b]) - int(qlens[b]) + t + 1 if spec else int(ctx[b])
+                s = []
+                for j in range(lim):
+                    blk, slot = rows[j]
+                    nope = sum(int(qn[tok, h, d]) * int(ckv[blk, slot, 0, d]) for d in range(512))
+                    rope = sum(float(qr[tok, h, d]) * float(kr[blk, slot, 0, d]) for d in range(64))
+                    s.append(float(scale) * (float(qkd[h]) * nope + rope))
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = sum(w)
+                o = [float(pvd[h]) * sum(w[j] * int(ckv[rows[j][0], rows[j][1], 0, d]) for j in range(lim)) / tot
+                     for d in range(512)]
+                out.append(o)
+                lse.append(m + math.log(tot))
+            tok += 1
+    return np.array(out), np.array(lse)
+
+
+@pytest.mark.parametrize("spec", [False, True])
+def test_mla_int8_brute_force(spec):
+    import workloads as W
+    qlens = [2, 3] if spec else None
+    c = W.make_mla_int8(61, [7, 12], qlens, 2, 4, "bf16", 1 if spec else 0, 1 if spec else 0, 0.07)
+    a = c.oracle_args()
+    ro, rl = oracle.mla(**a)
+    bo, bl = _brute_mla_int8(a["q_nope"], a["q_rope"], a["ct_kv"], a["k_rope"], a["block_tables"],
+                             a["context_lens"], qlens or [1, 1], 2, np.float32(0.07),
+                             np.float32(a["qk_descale"]), np.float32(a["pv_descale"]), spec)
+    np.testing.assert_allclose(ro.reshape(-1, 512), bo, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(rl.reshape(-1), bl, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_int8_descale_invariants():
+    import workloads as W
+    c = W.make_mla_int8(62, [40, 9, 130], None, 3, 16, "fp16", 0, 0, 0.07)
+    a = c.oracle_args()
+    o1, l1 = oracle.mla(**a)
+    # pvDescale scales the output linearly and leaves the LSE alone
+    a2 = dict(a, pv_descale=a["pv_descale"] * np.float32(2.0))
+    o2, l2 = oracle.mla(**a2)
+    np.testing.assert_allclose(o2, 2.0 * o1, rtol=1e-12, atol=0)
+    np.testing.assert_array_equal(l2, l1)
+    # qkDescale 0 leaves the rope part alone: the float oracle with qNope = 0, and
+    # pvDescale 1 reads ctKV as the values
+    a3 = dict(a, qk_descale=np.zeros(3, np.float32), pv_descale=np.ones(3, np.float32))
+    o3, l3 = oracle.mla(**a3)
+    a4 = dict(a, q_nope=np.zeros(a["q_nope"].shape), ct_kv=a["ct_kv"].astype(np.float64),
+              qk_descale=None, pv_descale=None)
+    o4, l4 = oracle.mla(**a4)
+    np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l3, l4, rtol=1e-12, atol=1e-12)

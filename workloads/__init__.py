@@ -19,6 +19,7 @@ from .gen import (  # noqa: F401
     make_prefill_config,
     make_mla,
     make_mla_config,
+    make_mla_int8,
     pad_prefill_case,
     PREFILL_CONFIGS,
     MLA_CONFIGS,

@@ -333,6 +333,8 @@ class MLACase:
     k_rope: Optional[torch.Tensor]      # [NB, BS, 1, 64] or None (cacheMode 0)
     block_tables: torch.Tensor          # int32 [B, maxBlockNum]
     kv_head_num: int = 1
+    qk_descale: Optional[np.ndarray] = None  # float32 [H], int8 cache only (q_nope, ct_kv int8)
+    pv_descale: Optional[np.ndarray] = None
 
     @property
     def batch(self):
@@ -368,7 +370,8 @@ class MLACase:
                     k_rope=npy(self.k_rope), block_tables=self.block_tables.cpu().numpy(),
                     context_lens=self.context_lens, q_seq_len=self.q_seq_len,
                     head_num=self.head_num, qk_scale=self.qk_scale,
-                    mask_type=self.mask_type, calc_type=self.calc_type)
+                    mask_type=self.mask_type, calc_type=self.calc_type,
+                    qk_descale=self.qk_descale, pv_descale=self.pv_descale)
 
 
 def make_mla(seed, context_lens, q_seq_len, head_num, block_size, dtype, mask_type,
@@ -404,6 +407,50 @@ def make_mla(seed, context_lens, q_seq_len, head_num, block_size, dtype, mask_ty
                    calc_type=calc_type, cache_mode=cache_mode, qk_scale=float(qk_scale),
                    q_nope=q_nope, q_rope=q_rope, ct_kv=ct_kv, k_rope=k_rope,
                    block_tables=torch.from_numpy(table))
+
+
+def make_mla_int8(seed, context_lens, q_seq_len, head_num, block_size, dtype, mask_type,
+                  calc_type, qk_scale, poison=False, max_block_num=None, name="custom", seed_val=None):
+    """An MLA call over an int8 latent cache: qNope and ctKV int8, drawn as
+    round(32 * N(0, 1)) clipped to [-127, 127] (a latent of std 0.5 quantised with
+    step 1/64), qRope / kRope N(0, 0.5^2) in ``dtype``, per-head descales
+    qkDescale = U(0.5, 1.5) / 64^2 and pvDescale = U(0.5, 1.5) / 64.  ``poison``
+    fills the cache slots the operator must not read with 127 (int8) and NaN
+    (kRope)."""
+    context_lens = np.asarray(context_lens, dtype=np.int32)
+    B = len(context_lens)
+    if calc_type == MLA_CALC_UNDEFINED:
+        qlens = np.ones(B, dtype=np.int32)
+        q_seq_len = None
+    else:
+        q_seq_len = np.asarray(q_seq_len, dtype=np.int32)
+        qlens = q_seq_len
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator("cpu").manual_seed(seed if seed_val is None else seed_val)
+    n_blocks, table, spare, need = _deal_blocks(rng, context_lens, block_size,
+                                                max_block_num=max_block_num)
+    T = int(qlens.sum())
+
+    def q8(shape):
+        return torch.randn(*shape, generator=gen).mul_(32.0).round_().clamp_(-127, 127).to(torch.int8)
+
+    q_nope = q8((T, head_num, 512))
+    q_rope = _randn(gen, (T, head_num, 64), 0.5, dtype)
+    ct_kv = q8((n_blocks, block_size, 1, 512))
+    k_rope = _randn(gen, (n_blocks, block_size, 1, 64), 0.5, dtype)
+    qk_descale = (rng.uniform(0.5, 1.5, size=head_num) / 64.0 ** 2).astype(np.float32)
+    pv_descale = (rng.uniform(0.5, 1.5, size=head_num) / 64.0).astype(np.float32)
+    if poison:
+        wide = ct_kv.view(torch.uint8)  # poison through a byte view: 127 in every unread slot
+        mark = torch.zeros(ct_kv.shape, dtype=torch.float32)
+        _poison_cache(mark, table, context_lens, need, spare, block_size)
+        wide[torch.isnan(mark)] = 127
+        _poison_cache(k_rope, table, context_lens, need, spare, block_size)
+    return MLACase(name=name, dtype=dtype, context_lens=context_lens, q_seq_len=q_seq_len,
+                   head_num=head_num, block_size=block_size, mask_type=mask_type,
+                   calc_type=calc_type, cache_mode=MLA_CACHE_KROPE_CTKV, qk_scale=float(qk_scale),
+                   q_nope=q_nope, q_rope=q_rope, ct_kv=ct_kv, k_rope=k_rope,
+                   block_tables=torch.from_numpy(table), qk_descale=qk_descale, pv_descale=pv_descale)
 
 
 def make_mla_config(name, poison=False, device=None):

@@ -688,14 +688,33 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
       s[0] = f32x16{};
       s[1] = f32x16{};
+      // K operand reads run kQkDepth MFMAs ahead; the next tile's loads sit
+      // between the MFMAs in one straight-line version (no branch between them)
+      // and are left out of the other (last iteration).
+      auto qk = [&](auto LOAD) __attribute__((always_inline)) {
+        auto rd = [&](int i) -> V8 {
+          const int c = i >> 1, kb = i & 1;
+          return *(const V8*)(lds + kB + qa[c >> 1] + 8320 * kb + 32 * (c & 1));
+        };
+        constexpr int kQkDepth = 4;
+        V8 ring[kQkDepth];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+        for (int i = 0; i < kQkDepth; ++i) ring[i] = rd(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const V8 a = *(const V8*)(lds + kB + qa[c >> 1] + 8320 * kb + 32 * (c & 1));
-          s[kb] = mfma32(a, qreg[c], s[kb]);
-          if (kb == 1) issue_next(c);
+        for (int i = 0; i < 2 * NC; ++i) {
+          const V8 a = ring[i % kQkDepth];
+          if (i + kQkDepth < 2 * NC) ring[i % kQkDepth] = rd(i + kQkDepth);
+          s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]);
+          if constexpr (decltype(LOAD)::value) {
+            if (i & 1) issue_block((i >> 1) & 1, 4 * w + (i >> 2), ((i >> 1) & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      if (load_next) {
+        qk(std::true_type{});
+      } else {
+        qk(std::false_type{});
       }
       // block id two iterations ahead, read while the softmax runs
       blk_next = block_of(u + 2);

@@ -357,3 +357,24 @@ def test_mla_int8_valid_args_reach_hip_or_succeed(lib):
     assert st in (0, 4), lib.mpaGetLastErrorMessage()
     if st == 0:
         assert lib.mpaDestroyOperation(op) == 0
+
+
+def test_prefill_plan_order_per_xcd():
+    """Within an XCD the plan keeps a group's items together unless running them
+    longest first ends the modelled schedule clearly earlier: the short-item GQA
+    prefix workload comes out longest first, the single long MHA sequence keeps
+    each head's items adjacent."""
+    import masked_paged_attention_amd as mpa
+    import workloads as W
+    c = W.make_prefill_config("prefix_gqa_causal")
+    items, _, _, _ = mpa.plan_prefill(c.seq_len, c.kv_seq_len, 9, 32, 8)
+    for x in range(8):
+        mine = items[x::8]
+        mine = mine[mine[:, 0] >= 0]
+        assert np.all(np.diff(mine[:, 3]) <= 0)
+    items, _, _, _ = mpa.plan_prefill([16384], [16384], 4, 40, 40)
+    for x in range(8):
+        mine = items[x::8]
+        heads = mine[mine[:, 0] >= 0][:, 1]
+        changes = int(np.count_nonzero(np.diff(heads)))
+        assert changes == len(set(heads.tolist())) - 1   # each head's items form one run

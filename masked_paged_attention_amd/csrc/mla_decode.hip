@@ -78,24 +78,30 @@ constexpr int kQ8PairBytes = 2 * kDv + 16;
 constexpr int kQ8LatBytes = 16 * kQ8PairBytes;
 __device__ __forceinline__ int q8_slot_byte(int s) { return kQ8PairBytes * (s & 15) + kDv * (s >> 4); }
 
-// 8 signed bytes -> 8 fp16 values, exact: byte x ^ 0x80 = x + 128 placed under
-// the fp16 exponent byte 0x64 is the value 1024 + (x + 128); subtracting 1152
-// leaves x.
-__device__ __forceinline__ f16x8 i8x8_to_f16x8(i32x2 t) {
+// 8 signed bytes -> the 8 fp16 values x + 1152, exact: byte x ^ 0x80 = x + 128
+// placed under the fp16 exponent byte 0x64 is the value 1024 + (x + 128).  The
+// bias is taken off the output once (1152 times the sum of the fp16 P that
+// multiplied it) instead of off every value.
+__device__ __forceinline__ f16x8 i8x8_biased_f16x8(i32x2 t) {
   const unsigned a = (unsigned)t[0] ^ 0x80808080u;
   const unsigned b = (unsigned)t[1] ^ 0x80808080u;
+  // v_perm_b32 byte selectors: 0-3 pick bytes of the second operand, 4-7 of the
+  // first (here the exponent byte 0x64), so each pair is one instruction.
+  constexpr unsigned kExp = 0x64646464u;
   u32x4 w;
-  w[0] = (a & 0xFFu) | ((a & 0xFF00u) << 8) | 0x64006400u;
-  w[1] = ((a >> 16) & 0xFFu) | ((a >> 8) & 0xFF0000u) | 0x64006400u;
-  w[2] = (b & 0xFFu) | ((b & 0xFF00u) << 8) | 0x64006400u;
-  w[3] = ((b >> 16) & 0xFFu) | ((b >> 8) & 0xFF0000u) | 0x64006400u;
-  const _Float16 k = (_Float16)1152.0f;
-  return __builtin_bit_cast(f16x8, w) - (f16x8){k, k, k, k, k, k, k, k};
+  w[0] = __builtin_amdgcn_perm(kExp, a, 0x04010400u);  // [a0, 0x64, a1, 0x64]
+  w[1] = __builtin_amdgcn_perm(kExp, a, 0x04030402u);  // [a2, 0x64, a3, 0x64]
+  w[2] = __builtin_amdgcn_perm(kExp, b, 0x04010400u);
+  w[3] = __builtin_amdgcn_perm(kExp, b, 0x04030402u);
+  return __builtin_bit_cast(f16x8, w);  // x + 1152, exact
 }
 
 // Q8: the int8 latent cache (qNope and ctKV int8, per-head descales) -- the
 // nope part of the scores on the int8 MFMA (exact integer products), the value
-// side through the 8-bit transpose read and an exact fp16 conversion.
+// side through the 8-bit transpose read and an exact conversion to fp16 values
+// biased by 1152; the output takes off 1152 times the row's sum of the fp16 P
+// (the fp32 accumulation error this adds is bounded by 2^-24 x 1279 x sum P per
+// MFMA accumulation step, far below the output rounding).
 template <typename T, bool ONE_BLOCK, bool Q8>
 __global__ void __launch_bounds__(512, 1)
     mla_split_kernel(MlaParams p, const int32_t* __restrict__ block_tables,
@@ -270,6 +276,7 @@ __global__ void __launch_bounds__(512, 1)
   V8 qreg[Q8 ? 1 : NCH];
   i32x4 qreg8[Q8 ? NCH8 : 1];
   float qk_desc = 1.0f, pv_desc = 1.0f, pv_desc_next = 1.0f;  // Q8: this lane's row's head
+  float l16_run = 0.0f;  // Q8: sum of the fp16-rounded P (the values carry a bias of 1152)
   f32x16 o[NDT];
   float m_run = -INFINITY, l_run = 0.0f;
   bool row_ok = false, w_active = false;
@@ -352,6 +359,7 @@ __global__ void __launch_bounds__(512, 1)
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     m_run = -INFINITY;
     l_run = 0.0f;
+    l16_run = 0.0f;
     pv_desc = pv_desc_next;
   };
 
@@ -455,7 +463,7 @@ __global__ void __launch_bounds__(512, 1)
       const T* vbase = lat + lat_slot(tr_row) * kLatRow + tr_col;
       auto load_v = [&](int i) -> PV8 {
         if constexpr (Q8) {
-          return i8x8_to_f16x8(lds_read_tr8(vbase8 + kDv * (i >> 3) + 32 * (i & 7)));
+          return i8x8_biased_f16x8(lds_read_tr8(vbase8 + kDv * (i >> 3) + 32 * (i & 7)));
         } else {
           const T* src0 = vbase + (i >> 3) * (16 * kLatRow) + 32 * (i & 7);
           const s16x4 lo = lds_read_tr16(src0);
@@ -508,6 +516,7 @@ __global__ void __launch_bounds__(512, 1)
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         l_run *= alpha;
+        if constexpr (Q8) l16_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
         m_run = m_new;
@@ -526,6 +535,12 @@ __global__ void __launch_bounds__(512, 1)
         p0[e] = (PT)s0[e];
         p1[e] = (PT)s0[8 + e];
       }
+      if constexpr (Q8) {
+        float q16 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q16 += (float)p0[e] + (float)p1[e];
+        l16_run += q16;
+      }
 #pragma unroll
       for (int i = 0; i < 2 * NDT; ++i) {
         const PV8 a = vring[i % kPvDepth];
@@ -541,6 +556,7 @@ __global__ void __launch_bounds__(512, 1)
   auto seg_end = [&](int seg) __attribute__((always_inline)) {
     if (!w_active) return;
     const float l_tot = sum_with_other_half(l_run);
+    const float bias = Q8 ? 1152.0f * sum_with_other_half(l16_run) : 0.0f;  // both halves take part
     if (!row_ok) return;
     const int4 sg = sload_int4(&segs[seg]);
     const int4 sq = sload_int4(&seqs[sg.x]);
@@ -566,7 +582,7 @@ __global__ void __launch_bounds__(512, 1)
       for (int q = 0; q < 4; ++q) {
         typename Vec<T>::x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * q + e] * inv);
+        for (int e = 0; e < 4; ++e) v[e] = (T)((o[dt][4 * q + e] - bias) * inv);
         *(typename Vec<T>::x4*)(orow + 32 * dt + 8 * q) = v;
       }
     }

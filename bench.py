@@ -144,11 +144,17 @@ def short_kernel_name(mangled):
                                 m.group(1) if m.group(1) else ("true" if m.group(2) == "1" else "false"))
             elif rest.startswith("<"):  # demangled
                 inner = rest[1:rest.find(">")] if ">" in rest else ""
-                for a in inner.split(","):
-                    a = a.strip()
-                    if a in ("bool", "E"):  # pieces of a garbled non-type argument
+                parts = [a.strip() for a in inner.split(",")]
+                i = 0
+                while i < len(parts):
+                    a = parts[i]
+                    i += 1
+                    # rocprofv3 prints the mangled __bf16 (DF16b) as "bool _Accum" and
+                    # the mangled true (Lb1E) as the two pieces "bool", "E"
+                    if a == "bool" and i < len(parts) and parts[i] == "E":
+                        args.append("true")
+                        i += 1
                         continue
-                    # (rocprofv3 prints the mangled __bf16, DF16b, as "bool _Accum")
                     args.append("bf16" if "bf" in a.lower() or "_Accum" in a else
                                 "fp16" if "16" in a and "float" in a.lower() else a)
             return key + ("<" + ",".join(args) + ">" if args else "")

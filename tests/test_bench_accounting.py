@@ -77,7 +77,10 @@ def test_short_kernel_names_bool_and_demangled():
         "_ZN3mpa12_GLOBAL__N_116mla_split_kernelIDF16bLb1EEEvNS_9MlaParamsEPKi") == "mla_split_kernel<bf16,true>"
     assert bench.short_kernel_name(
         "void mpa::(anonymous namespace)::mla_split_kernel<bool _Accum, bool, E>(mpa::MlaParams)") == \
-        "mla_split_kernel<bf16>"
+        "mla_split_kernel<bf16,true>"
+    assert bench.short_kernel_name(
+        "void mpa::(anonymous namespace)::mla_split_kernel<bool _Accum, bool, E, false>(mpa::MlaParams)") == \
+        "mla_split_kernel<bf16,true,false>"
 
 
 def test_short_kernel_name_of_the_dma_prefill_kernel():

@@ -79,3 +79,15 @@ def test_row_hidden_by_the_tile_is_zero():
     ro, rl = oracle.prefix_encoder(**c.oracle_args())
     assert np.abs(out[keep].float().cpu().numpy() - ro[keep.numpy()]).max() <= 5e-3
     assert np.all(np.isneginf(rl[5]))
+
+
+@pytest.mark.parametrize("name", ["prefix_gqa_causal", "alibi_right_4x4096"])
+def test_compressed_mask_full_size_sampled(name):
+    # the bench's compressed-tile calls: the full workloads with the page's tile
+    log(f"case compressed full-size {name} (sampled rows)")
+    from tests.gpu_helpers import check_prefill_sampled
+    c = W.make_prefill_config(name, poison=True)
+    c = dataclasses.replace(c, mask_tile=W.compressed_tile(c.mask_type, c.dtype)).to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_sampled(c, out, lse, n=160, seed=11)
+    assert torch.isfinite(out.float()).all()

@@ -185,3 +185,12 @@ def test_chunked_mask_with_a_long_chunk_equals_causal():
     import dataclasses
     o2, l2 = gpu_prefill(dataclasses.replace(c, chunk=0))
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_chunked_full_size_sampled():
+    # the bench's chunked call: one 16384-token bf16 sequence, 40 heads, chunk 2048
+    log("case chunked full-size 16384 chunk 2048 (sampled rows)")
+    c = W.make_prefill(87, np.array([16384]), np.array([16384]), 40, 40, 128, 128, "bf16", 9,
+                       1.0 / np.sqrt(128.0), poison=True, chunk=2048).to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_sampled(c, out, lse, n=160, seed=12)

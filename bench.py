@@ -255,7 +255,8 @@ def time_op(torch, run, iters, warmup):
 
 def cpu_baseline(budget_s=12.0):
     """The fp64 oracle, as it is, on a bounded sample of the prefill workload: whole
-    (sequence, head) pairs in a seeded order until the time budget is spent."""
+    (sequence, head) pairs in a seeded order, passing over the workload again when
+    it is done, until the time budget is spent."""
     import oracle
     import workloads as W
     try:
@@ -271,20 +272,22 @@ def cpu_baseline(budget_s=12.0):
     done_flops = 0
     done = 0
     t0 = time.perf_counter()
-    for k in order:
-        b, h = pairs[k]
-        L = int(c.seq_len[b])
-        rows = [(b, i, h) for i in range(L)]
-        oracle.prefix_encoder_rows(rows=rows, **args)
-        done_flops += prefill_valid_flops([L], [c.kv_seq_len[b]], True, 1, c.head_size)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 <= budget_s:
+        for k in order:
+            b, h = pairs[k]
+            L = int(c.seq_len[b])
+            rows = [(b, i, h) for i in range(L)]
+            oracle.prefix_encoder_rows(rows=rows, **args)
+            done_flops += prefill_valid_flops([L], [c.kv_seq_len[b]], True, 1, c.head_size)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{done} of {len(pairs)} (sequence, head) pairs of the prefix-encoder GQA "
-                      f"workload, all rows each, fp64 numpy, {dt:.1f} s"}
+            "sample": f"{done} (sequence, head) pairs of the prefix-encoder GQA workload "
+                      f"({len(pairs)} per pass, {done / len(pairs):.1f} passes), all rows each, "
+                      f"fp64 numpy, {dt:.1f} s"}
 
 
 def _sum_or_none(*xs):

@@ -675,10 +675,9 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
   if (m >= rows) return;
   const int l = threadIdx.x & 63;
   const long long base = (long long)sq2.x + m;  // partial row of segment k: base + k * rows
-  float mx = -INFINITY;
-  for (int k = l; k < n; k += 64) mx = fmaxf(mx, p.part_lse[base + (long long)k * rows]);
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  const float mref = (mx == -INFINITY) ? 0.0f : mx;
+  // One pass, 8 segments at a time (one memory round trip per group), the sum and
+  // the accumulator kept relative to the running max mref.
+  float mref = -INFINITY;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float tot = 0.0f;
   for (int k0 = 0; k0 < n; k0 += 8) {
@@ -696,13 +695,22 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
         for (int e = 0; e < 8; ++e) a[u][e] = (T)0.0f;
       }
     }
+    float gm = mref;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gm = fmaxf(gm, wgt[u]);
+    if (gm == -INFINITY) continue;  // nothing seen so far
+    const float sc = fast_exp2(mref - gm);  // 0 while mref = -inf
+    tot *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float wu = fast_exp2(wgt[u] - mref);
+      const float wu = fast_exp2(wgt[u] - gm);
       tot += wu;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += wu * (float)a[u][e];
     }
+    mref = gm;
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   typename Vec<T>::x8 v;

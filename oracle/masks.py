@@ -16,8 +16,7 @@ prefix plus the new rows, ATB page "PrefixEncoder", parameter table, rows seqLen
 and kvSeqLen).  Query row i sits at absolute position a_i = (kv_len - seq_len) + i;
 key j sits at position j.
 
-Readings taken where the pages are silent, garbled or lost (each is listed in
-the design doc's ambiguity register):
+Readings taken where the pages are silent, garbled or lost:
 
 * masked pairs are excluded exactly (weight 0), i.e. -inf semantics -- the nalar.dev
   article, section "Masking mengubah kelayakan relasi attention", allows either a

@@ -1,6 +1,6 @@
 """Seeded generators for the prefill (PrefixEncoder) and MLA decode workloads.
 
-Recipe (also stated in the design doc):
+Recipe:
 
 * lengths and the block permutation come from ``numpy.random.default_rng(seed_len)``;
 * values are fp32 ``torch.randn`` from ``torch.Generator('cpu').manual_seed(seed_val)``,

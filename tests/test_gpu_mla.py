@@ -170,3 +170,15 @@ def test_int8_prefill_and_determinism():
     check_mla(c, o1, l1)
     o2, l2 = gpu_mla(c)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_long_context_sampled():
+    # contexts up to 64K keys next to short ones
+    log("case mla long contexts (sampled rows)")
+    ctx = [65536, 300, 40000, 1]
+    c = W.make_mla(95, ctx, None, 64, 128, "bf16", 0, 0, 1, 1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(8)
+    rows = sorted({(int(rng.integers(len(ctx))), int(rng.integers(64))) for _ in range(64)} |
+                  {(b, h) for b in range(len(ctx)) for h in (0, 63)})
+    check_mla(c, out, lse, rows=rows)

@@ -194,3 +194,14 @@ def test_chunked_full_size_sampled():
                        1.0 / np.sqrt(128.0), poison=True, chunk=2048).to(DEV)
     out, lse = gpu_prefill(c)
     check_prefill_sampled(c, out, lse, n=160, seed=12)
+
+
+@pytest.mark.parametrize("mask", [9, 3])
+def test_long_prefix_sampled(mask):
+    # a ~60K-key cached prefix: large block-table indices and offsets
+    log(f"case prefill long prefix mask={mask} (sampled rows)")
+    slopes = "alibi" if mask == 3 else None
+    c = W.make_prefill(93, np.array([700, 33]), np.array([60000, 40000]), 8, 2, 128, 128, "bf16", mask,
+                       1.0 / np.sqrt(128.0), slopes=slopes, poison=True).to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_sampled(c, out, lse, n=96, seed=13)

@@ -112,7 +112,10 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   const bool w_active = wrow0 < L;
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
   const int w_keys = keys_to(w_rows_end);
-  const int w_full_keys = kTile ? 0 : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+  // (norm tile: keys in 128-blocks before the first row's block have bias 0 for
+  // every row; the ALiBi tiles are read for every key)
+  const int w_full_keys = kTile ? (kType == 9 ? min(kv, (prefix + wrow0) / kMaskTile * kMaskTile) : 0)
+                                : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
   // Chunked mask: row a sees keys from lo(a) = chunk * floor(a / chunk) on; the
   // item starts at the tile of its first row's lo, a wave skips the tiles below
   // its first row's lo, and a tile below its last row's lo needs the predicate.
@@ -245,9 +248,11 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
     int dk = 0;
     if constexpr (kTile) {
       dk = a_bq - j0 / kMaskTile;
-      const T* src = (dk == 0 ? mrow_diag : mrow_back) + (j0 & (kMaskTile - 1));
+      if (j0 + kBN > w_full_keys) {  // tiles every row sees with bias 0 read nothing
+        const T* src = (dk == 0 ? mrow_diag : mrow_back) + (j0 & (kMaskTile - 1));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) mv[u] = *(const V4*)(src + 8 * u);
+        for (int u = 0; u < 8; ++u) mv[u] = *(const V4*)(src + 8 * u);
+      }
     }
     if (t + 1 < n_tiles) {
       load_tile(j0 + kBN, blk_next);
@@ -286,7 +291,10 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
           for (int r = 0; r < 16; ++r) {
             const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
             float x;
-            if constexpr (kTile) {
+            if constexpr (kTile && !decltype(with_mask)::value) {
+              // a tile every row sees with bias 0 (norm tile only)
+              x = __builtin_fmaf(s[kb][r], scale2, -m_ref);
+            } else if constexpr (kTile) {
               const float mval = (float)mv[4 * kb + (r >> 2)][r & 3];
               bool hide = dk < 0 || mval == -INFINITY;
               float bias2;  // bias in log2 units

@@ -433,6 +433,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   using V8 = typename Vec<T>::x8;
   using V4 = typename Vec<T>::x4;
   constexpr int D = 128;
+  constexpr bool kTile = (MASK & kMaskTileFlag) != 0;  // compressed norm tile read from p.mask
+  static_assert(!kTile || (MASK & 15) == 9, "the DMA kernel reads the norm tile only");
   constexpr bool kCausal = MASK != 0;
   constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
   constexpr bool kAlibiSqrt = MASK == 4;
@@ -473,7 +475,14 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const unsigned kv_row_bytes = (unsigned)p.kv_head_num * (unsigned)kRowBytes;
 
   const int item_rows_end = min(L, row0 + rows_per_item);
-  const int wg_keys = kCausal ? min(kv, prefix + item_rows_end) : kv;
+  // Norm tile: keys run to the end of the last row's 128-block (the tile decides
+  // inside the diagonal block); keys in blocks before the first row's block have
+  // bias 0 for every row.
+  auto keys_to = [&](int rows_end) {
+    const int a_last = prefix + rows_end - 1;
+    return kTile ? min(kv, (a_last / kMaskTile + 1) * kMaskTile) : kCausal ? min(kv, a_last + 1) : kv;
+  };
+  const int wg_keys = keys_to(item_rows_end);
   const int n_end = (wg_keys + kBN - 1) / kBN;
   // Chunked mask: row a sees keys from lo(a) = chunk * floor(a / chunk) on; the
   // item starts at the tile of its first row's lo.
@@ -482,9 +491,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const int n_tiles = n_end - t_lo;  // iterations
   const bool w_active = wrow0 < L;
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
-  const int w_keys = kCausal ? min(kv, prefix + w_rows_end) : kv;
+  const int w_keys = keys_to(w_rows_end);
   const int w_tiles = w_active ? (w_keys + kBN - 1) / kBN : 0;  // tiles 0 .. w_tiles-1 matter here
-  const int w_full_keys = kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+  const int w_full_keys = kTile ? min(kv, (prefix + wrow0) / kMaskTile * kMaskTile)
+                              : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
   const int w_t_lo = chunk_lo(prefix + wrow0) / kBN;                       // first tile the wave sees
   const int w_lo_last = chunk_lo(prefix + max(wrow0, w_rows_end - 1));   // below it: predicate
 
@@ -564,12 +574,26 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
   const float scale2 = p.scale2;
 
+  // Norm tile entries of this lane's query row for a tile that needs them: 8
+  // runs of 4 (row a mod 128, the tile's 64 columns); dk = the row's 128-block
+  // minus the key's.
+  V4 mtv[8];
+  int mdk = 0;
+  const T* mrow = nullptr;
+  if constexpr (kTile) mrow = (const T*)p.mask + (long long)(a_lane % kMaskTile) * p.mask_stride + 4 * g;
+  auto load_tile_mask = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * kBN;
+    mdk = a_lane / kMaskTile - j0 / kMaskTile;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(mrow + (j0 & (kMaskTile - 1)) + 8 * u);
+  };
+
   // P of tile t from S^T (in s): running max and sum (see the comment above).
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * kBN;
     const int dbase = a_lane - j0 - 4 * g;
     const int klim = kv - j0 - 4 * g;
-    const int vlim = kCausal ? min(klim, dbase + 1) : klim;
+    const int vlim = kCausal && !kTile ? min(klim, dbase + 1) : klim;
     const int llim = chunk_lo(a_lane) - j0 - 4 * g;  // chunked: key >= lo(a)  <=>  C >= llim
     const bool partial = j0 + kBN > w_full_keys || (kChunked && j0 < w_lo_last);
     const float dbf = (float)dbase;
@@ -616,6 +640,14 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           for (int r = 0; r < 16; ++r) {
             const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
             float v = score(kb, r, m_ref, nbm);
+            if constexpr (kTile && decltype(with_mask)::value) {
+              // diagonal block: the tile's entry (-inf hides the key); later
+              // blocks: hidden; earlier blocks: bias 0
+              const float mval = (float)mtv[4 * kb + (r >> 2)][r & 3];
+              const bool hide = mdk < 0 || (mdk == 0 && mval == -INFINITY);
+              v = mdk == 0 ? v + mval * kLog2e : v;
+              v = hide ? -INFINITY : v;
+            }
             if constexpr (decltype(with_mask)::value)
               v = (C < vlim && (!kChunked || C >= llim)) ? v : -INFINITY;
             x[kb][r] = v;
@@ -694,6 +726,11 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
     };
     if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
+      // tile entries first (their wait before the softmax also covers the next
+      // tile's loads issued below: only the tiles from the first row's block on)
+      if constexpr (kTile) {
+        if (t * kBN + kBN > w_full_keys) load_tile_mask(t);
+      }
       s[0] = f32x16{};
       s[1] = f32x16{};
       // K operand reads run kQkDepth MFMAs ahead; the next tile's loads sit
@@ -757,7 +794,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const float l_tot = sum_with_other_half(l_run);
   const int i = wrow0 + lq;
   if (i >= L) return;
-  const float inv = 1.0f / l_tot;
+  // A row whose tile hides every key gets O = 0 (and LSE = -inf).
+  const float inv = kTile && l_tot == 0.0f ? 0.0f : 1.0f / l_tot;
   T* orow = (T*)p.out + (qs + i) * q_row_stride + (long long)head * D + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -779,8 +817,11 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
-  if (D == 128 && p.bs_shift >= 6 && (mask_type & kMaskTileFlag) == 0) {
+  if (D == 128 && p.bs_shift >= 6 && ((mask_type & kMaskTileFlag) == 0 || mask_type == (kMaskTileFlag | 9))) {
     switch (mask_type) {
+      case kMaskTileFlag | 9:
+        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 9>), g, blk, 0, s, p, p.block_tables);
+        break;
       case 0: hipLaunchKernelGGL((prefill_dma_kernel<T, 0>), g, blk, 0, s, p, p.block_tables); break;
       case 3: hipLaunchKernelGGL((prefill_dma_kernel<T, 3>), g, blk, 0, s, p, p.block_tables); break;
       case 4: hipLaunchKernelGGL((prefill_dma_kernel<T, 4>), g, blk, 0, s, p, p.block_tables); break;

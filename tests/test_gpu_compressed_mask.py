@@ -91,3 +91,23 @@ def test_compressed_mask_full_size_sampled(name):
     out, lse = gpu_prefill(c)
     check_prefill_sampled(c, out, lse, n=160, seed=11)
     assert torch.isfinite(out.float()).all()
+
+
+def test_row_hidden_by_the_tile_is_zero_dma_path():
+    # the same with headSize 128 and 128-key blocks (the direct-load kernel)
+    log("case compressed norm tile with an empty row, headSize 128")
+    tile = W.compressed_tile(9, "bf16")
+    tile[5, :] = float("-inf")
+    c = W.make_prefill(241, np.array([40, 200]), np.array([40, 300]), 8, 2, 128, 128, "bf16", 9,
+                       1.0 / np.sqrt(128), poison=True, name="empty-row-128")
+    c = dataclasses.replace(c, mask_tile=tile).to(DEV)
+    out, lse = gpu_prefill(c)
+    assert torch.all(out[5] == 0)
+    assert torch.all(torch.isneginf(lse[5]))
+    import oracle
+    ro, rl = oracle.prefix_encoder(**c.oracle_args())
+    keep = np.ones(240, dtype=bool)
+    keep[5] = False
+    assert np.abs(out.float().cpu().numpy()[keep] - ro[keep]).max() <= 2e-2
+    l = lse.cpu().numpy()[keep]
+    assert (np.abs(l - rl[keep]) / np.maximum(1.0, np.abs(rl[keep]))).max() <= 1e-3

@@ -9,8 +9,8 @@
 //   s_j = qkScale * q.k_j + bias(a, j) over visible keys j,  o = softmax(s) V,
 //   lse = ln sum_j exp(s_j).
 // Visibility and bias are generated in registers from (maskType, slopes,
-// seqLen, kvSeqLen); the register-staged kernel can instead read them from an
-// explicit compressed mask tile (ATB page "压缩mask", section 约束说明).
+// seqLen, kvSeqLen), or read from an explicit compressed mask tile (ATB page
+// "压缩mask", section 约束说明) by either kernel.
 //
 // Shape of one workgroup (256 threads = 4 waves of 64):
 //   * each wave owns 32 query rows of one head; the heads of one KV group share
@@ -433,13 +433,14 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   using V8 = typename Vec<T>::x8;
   using V4 = typename Vec<T>::x4;
   constexpr int D = 128;
-  constexpr bool kTile = (MASK & kMaskTileFlag) != 0;  // compressed norm tile read from p.mask
-  static_assert(!kTile || (MASK & 15) == 9, "the DMA kernel reads the norm tile only");
-  constexpr bool kCausal = MASK != 0;
-  constexpr bool kAlibiLinear = MASK == 3 || MASK == 5;
-  constexpr bool kAlibiSqrt = MASK == 4;
-  constexpr bool kReverse = kAlibiLinear || kAlibiSqrt;
-  constexpr bool kChunked = MASK == 10;   // causal inside chunks of p.chunk keys
+  constexpr int kType = MASK & 15;        // maskType (0, 3, 4, 5, 9) or 10 (chunked)
+  constexpr bool kTile = (MASK & kMaskTileFlag) != 0;  // bias read from a compressed tile (p.mask)
+  constexpr bool kCausal = kType != 0;
+  constexpr bool kAlibiLinear = !kTile && (kType == 3 || kType == 5);  // generated ALiBi bias
+  constexpr bool kAlibiSqrt = !kTile && kType == 4;
+  constexpr bool kTileAlibi = kTile && (kType == 3 || kType == 4 || kType == 5);
+  constexpr bool kReverse = kType == 3 || kType == 4 || kType == 5;
+  constexpr bool kChunked = kType == 10;  // causal inside chunks of p.chunk keys
   constexpr int NC = D / 16;              // 16-wide contraction chunks of QK^T
   constexpr int NDT = D / 32;             // 32-row tiles of O^T
   constexpr int kRowBytes = D * (int)sizeof(T);   // 256
@@ -475,9 +476,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const unsigned kv_row_bytes = (unsigned)p.kv_head_num * (unsigned)kRowBytes;
 
   const int item_rows_end = min(L, row0 + rows_per_item);
-  // Norm tile: keys run to the end of the last row's 128-block (the tile decides
-  // inside the diagonal block); keys in blocks before the first row's block have
-  // bias 0 for every row.
+  // Compressed tile: keys run to the end of the last row's 128-block (the tile
+  // decides inside the diagonal block).
   auto keys_to = [&](int rows_end) {
     const int a_last = prefix + rows_end - 1;
     return kTile ? min(kv, (a_last / kMaskTile + 1) * kMaskTile) : kCausal ? min(kv, a_last + 1) : kv;
@@ -493,8 +493,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const int w_rows_end = min(L, wrow0 + kRowsPerWave);
   const int w_keys = keys_to(w_rows_end);
   const int w_tiles = w_active ? (w_keys + kBN - 1) / kBN : 0;  // tiles 0 .. w_tiles-1 matter here
+  // (compressed tiles: keys in 128-blocks before the first row's block are
+  // behind every row's diagonal block)
   const int w_full_keys = kTile ? min(kv, (prefix + wrow0) / kMaskTile * kMaskTile)
-                              : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
+                                : kCausal ? min(kv, prefix + wrow0 + 1) : kv;
   const int w_t_lo = chunk_lo(prefix + wrow0) / kBN;                       // first tile the wave sees
   const int w_lo_last = chunk_lo(prefix + max(wrow0, w_rows_end - 1));   // below it: predicate
 
@@ -571,21 +573,44 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   float l_run = 0.0f;
   const int a_lane = prefix + wrow0 + lq;
   float slope2 = 0.0f;
-  if constexpr (kAlibiLinear || kAlibiSqrt) slope2 = p.slopes[head] * kLog2e;
+  if constexpr (kAlibiLinear || kAlibiSqrt || kTileAlibi) slope2 = p.slopes[head] * kLog2e;
   const float scale2 = p.scale2;
 
-  // Norm tile entries of this lane's query row for a tile that needs them: 8
-  // runs of 4 (row a mod 128, the tile's 64 columns); dk = the row's 128-block
-  // minus the key's.
+  // Compressed tile entries of this lane's query row for a key tile that needs
+  // them: 8 runs of 4 (the tile's 64 columns) from row r = a mod 128 (the key in
+  // the row's own 128-block) or 128 + r (a key dk >= 1 blocks behind: ALiBi
+  // tiles); dk = the row's 128-block minus the key's.  The norm tile is read
+  // for the few tiles from the first row's block on, at the start of their
+  // iteration; the ALiBi tiles for every tile, one iteration ahead, so that the
+  // wait that ends an iteration has them in place and none is needed before
+  // the softmax (it would drain the next tile's direct loads).
   V4 mtv[8];
   int mdk = 0;
-  const T* mrow = nullptr;
-  if constexpr (kTile) mrow = (const T*)p.mask + (long long)(a_lane % kMaskTile) * p.mask_stride + 4 * g;
+  // ALiBi tiles: the block shift of this tile's entries (times slope2 for the
+  // linear types)
+  float mshift = 0.0f;
+  const int a_bq = a_lane / kMaskTile;
+  const T* mrow_diag = nullptr;
+  const T* mrow_back = nullptr;
+  if constexpr (kTile) {
+    mrow_diag = (const T*)p.mask + (long long)(a_lane - a_bq * kMaskTile) * p.mask_stride + 4 * g;
+    mrow_back = kType == 9 ? mrow_diag : mrow_diag + (long long)kMaskTile * p.mask_stride;
+  }
+  auto needs_tile_mask = [&](int t) { return kTileAlibi || (kTile && t * kBN + kBN > w_full_keys); };
   auto load_tile_mask = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * kBN;
-    mdk = a_lane / kMaskTile - j0 / kMaskTile;
+    mdk = a_bq - j0 / kMaskTile;
+    // right ALiBi: y - 128 (dk - 1) behind the diagonal block; left ALiBi:
+    // y - 128 dk (relative to the row's block origin)
+    if constexpr (kType == 5) {
+      mshift = -slope2 * (float)(kMaskTile * mdk);
+    } else if constexpr (kTileAlibi) {
+      mshift = mdk > 0 ? -(float)(kMaskTile * (mdk - 1)) : 0.0f;
+      if constexpr (kType == 3) mshift *= slope2;
+    }
+    const T* src = (mdk == 0 ? mrow_diag : mrow_back) + (j0 & (kMaskTile - 1));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(mrow + (j0 & (kMaskTile - 1)) + 8 * u);
+    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(src + 8 * u);
   };
 
   // P of tile t from S^T (in s): running max and sum (see the comment above).
@@ -599,12 +624,27 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     const float dbf = (float)dbase;
     float x[2][16];
     float psum;
-    auto score = [&](int kb, int r, float m_ref, float nbm) __attribute__((always_inline)) -> float {
+    // (checked: ALiBi tiles select -inf for a -inf entry; the unchecked form,
+    // used by the fast path, gets -inf from it for a positive slope, and NaN or
+    // +inf otherwise, which fail that path's sum test and send the tile to the
+    // checked path)
+    auto score = [&](int kb, int r, float m_ref, float nbm, bool checked) __attribute__((always_inline)) -> float {
       const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
       if constexpr (kAlibiLinear) {
         return __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
       } else if constexpr (kAlibiSqrt) {
         return __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
+      } else if constexpr (kTileAlibi) {
+        // the tile's entry y (+ block shift) as slope y, or -slope sqrt(-y);
+        // a -inf entry hides the key
+        const float mval = (float)mtv[4 * kb + (r >> 2)][r & 3];
+        float v;
+        if constexpr (kType == 4) {
+          v = __builtin_fmaf(-slope2, fast_sqrt(-mval - mshift), __builtin_fmaf(s[kb][r], scale2, -m_ref));
+        } else {
+          v = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, mval, mshift - m_ref));
+        }
+        return checked && mval == -INFINITY ? -INFINITY : v;
       } else {
         return __builtin_fmaf(s[kb][r], scale2, -m_ref);
       }
@@ -617,7 +657,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(score(kb, r, m_run, nbm));
+          const float e = fast_exp2(score(kb, r, m_run, nbm, false));
           x[kb][r] = e;
           ps[r & 3] += e;
         }
@@ -639,15 +679,16 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
-            float v = score(kb, r, m_ref, nbm);
-            if constexpr (kTile && decltype(with_mask)::value) {
-              // diagonal block: the tile's entry (-inf hides the key); later
-              // blocks: hidden; earlier blocks: bias 0
+            float v = score(kb, r, m_ref, nbm, true);
+            if constexpr (kType == 9 && kTile && decltype(with_mask)::value) {
+              // norm tile: the entry in the diagonal block (-inf hides the
+              // key), 0 behind it, later blocks hidden
               const float mval = (float)mtv[4 * kb + (r >> 2)][r & 3];
               const bool hide = mdk < 0 || (mdk == 0 && mval == -INFINITY);
               v = mdk == 0 ? v + mval * kLog2e : v;
               v = hide ? -INFINITY : v;
             }
+            if constexpr (kTileAlibi && decltype(with_mask)::value) v = mdk < 0 ? -INFINITY : v;
             if constexpr (decltype(with_mask)::value)
               v = (C < vlim && (!kChunked || C >= llim)) ? v : -INFINITY;
             x[kb][r] = v;
@@ -702,6 +743,9 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   // landed too, so no wait for Q is left for it to place inside the loop,
   // where it would also drain the tile loads in flight).
   int blk_next = block_of(1);  // block id of the next iteration's tile
+  if constexpr (kTileAlibi) {
+    if (w_active) load_tile_mask(tile_of(0));
+  }
   {
     const TileSrc ts = tile_src(0, block_of(0));
 #pragma unroll
@@ -726,10 +770,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
     };
     if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
-      // tile entries first (their wait before the softmax also covers the next
-      // tile's loads issued below: only the tiles from the first row's block on)
-      if constexpr (kTile) {
-        if (t * kBN + kBN > w_full_keys) load_tile_mask(t);
+      if constexpr (kType == 9 && kTile) {
+        // (their wait before the softmax also covers the next tile's loads
+        // issued below: only the tiles from the first row's block on)
+        if (needs_tile_mask(t)) load_tile_mask(t);
       }
       s[0] = f32x16{};
       s[1] = f32x16{};
@@ -764,6 +808,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       // block id two iterations ahead, read while the softmax runs
       blk_next = block_of(u + 2);
       softmax(t);
+      // the next key tile's ALiBi tile entries (this tile's are consumed)
+      if constexpr (kTileAlibi) {
+        if (u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));
+      }
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -779,6 +827,9 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
       blk_next = block_of(u + 2);
+      if constexpr (kTileAlibi) {
+        if (w_active && u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));
+      }
     }
     // The next tile has landed (each wave waits for its own loads; the barrier
     // publishes them and ends every read of this buffer).
@@ -809,7 +860,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   }
   if (p.lse != nullptr && g == 0) {
     float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if constexpr (MASK == 5) lse += p.slopes[head] * (float)a_lane;
+    if constexpr (kType == 5) lse += p.slopes[head] * (float)(kTile ? a_bq * kMaskTile : a_lane);
     p.lse[(qs + i) * p.head_num + head] = lse;
   }
 }
@@ -817,8 +868,17 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
-  if (D == 128 && p.bs_shift >= 6 && ((mask_type & kMaskTileFlag) == 0 || mask_type == (kMaskTileFlag | 9))) {
+  if (D == 128 && p.bs_shift >= 6) {
     switch (mask_type) {
+      case kMaskTileFlag | 3:
+        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 3>), g, blk, 0, s, p, p.block_tables);
+        break;
+      case kMaskTileFlag | 4:
+        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 4>), g, blk, 0, s, p, p.block_tables);
+        break;
+      case kMaskTileFlag | 5:
+        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 5>), g, blk, 0, s, p, p.block_tables);
+        break;
       case kMaskTileFlag | 9:
         hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 9>), g, blk, 0, s, p, p.block_tables);
         break;

@@ -181,7 +181,8 @@ def compressed_bias(mask_type, tile, slope, a, j, kv_len):
         shift = np.where(k >= 1, -TILE * (k - 1), 0).astype(np.float64)
         val = np.where(k >= 0, val + shift, -np.inf)
         if mask_type == MASK_ALIBI:
-            out = np.where(np.isfinite(val), slope * val, -np.inf)
+            with np.errstate(invalid="ignore"):  # slope 0 times a -inf entry (not selected)
+                out = np.where(np.isfinite(val), slope * val, -np.inf)
         else:
             dist = -val
             with np.errstate(invalid="ignore"):
@@ -194,7 +195,8 @@ def compressed_bias(mask_type, tile, slope, a, j, kv_len):
         val = tile[rows, cols]
         # The tile holds the in-tile column; the key tile's origin is added back.
         val = np.where(k >= 0, val + TILE * bk, -np.inf)
-        out = np.where(np.isfinite(val), slope * val, -np.inf)
+        with np.errstate(invalid="ignore"):  # slope 0 times a -inf entry (not selected)
+            out = np.where(np.isfinite(val), slope * val, -np.inf)
     else:
         raise ValueError(f"mask type {mask_type} has no compressed form")
     return np.where(j < kv_len, out, -np.inf)

@@ -111,3 +111,16 @@ def test_row_hidden_by_the_tile_is_zero_dma_path():
     assert np.abs(out.float().cpu().numpy()[keep] - ro[keep]).max() <= 2e-2
     l = lse.cpu().numpy()[keep]
     assert (np.abs(l - rl[keep]) / np.maximum(1.0, np.abs(rl[keep]))).max() <= 1e-3
+
+
+@pytest.mark.parametrize("mask_type", [3, 4, 5])
+def test_alibi_tile_zero_and_negative_slopes(mask_type):
+    # heads with slope 0 and negative slopes: a -inf entry still hides its key
+    # (slope * -inf is not -inf there), headSize 128 and 128-key blocks
+    log(f"case compressed ALiBi tile mask={mask_type} with zero / negative slopes")
+    slopes = np.array([0.5, 0.0, -0.03125, 0.125, 0.0, 0.0625, -0.0078125, 0.25], dtype=np.float32)
+    c = W.make_prefill(250 + mask_type, np.array([300, 129]), np.array([700, 129]), 8, 2, 128, 128, "bf16",
+                       mask_type, 1.0 / np.sqrt(128), slopes=slopes, poison=True, name=f"slopes{mask_type}")
+    c = dataclasses.replace(c, mask_tile=W.compressed_tile(mask_type, "bf16", 31)).to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)

@@ -10,8 +10,10 @@ One step = one pass of the whole path over one batch of synthetic input:
     is cold.
 value = valid prefill FLOPs (4 * headSize per visible (query, key) pair) / prefill
 kernel time; the decode rate (algorithmic bytes / MLA call time) is reported
-beside it.  Kernel times come from HIP events recorded on the launch stream
-around each launch inside the timed region.
+beside it.  Kernel times come from HIP events that each call records on its own
+kernels' dispatch packets (start of its first kernel, end of its last) inside the
+timed region, so no event command sits between the kernels on the stream; the
+step time comes from two stream events around the whole timed region.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
 """
@@ -240,7 +242,8 @@ def _events(torch):
 
 
 def time_op(torch, run, iters, warmup):
-    """Average ms of run() over iters launches, events on the current stream."""
+    """Average ms of run() over iters launches, events on the current stream (for
+    calls without an operation object)."""
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -250,6 +253,35 @@ def time_op(torch, run, iters, warmup):
         run()
         b.record()
     torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def launch_events(torch, n):
+    """n pairs of timing events, created (HIP events exist only after a first record)."""
+    evs = [_events(torch) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def time_ops(torch, ops, iters, warmup):
+    """Average ms of one call over iters back-to-back calls of the operations in turn,
+    from events recorded on each call's own kernels (its first kernel's start, its
+    last kernel's end: mpaOperationSetLaunchEvents), so no command sits between the
+    calls on the stream."""
+    for i in range(warmup):
+        ops[i % len(ops)].run()
+    torch.cuda.synchronize()
+    evs = launch_events(torch, iters)
+    for i, (a, b) in enumerate(evs):
+        op = ops[i % len(ops)]
+        op.set_launch_events(a, b)
+        op.run()
+    torch.cuda.synchronize()
+    for op in ops:
+        op.set_launch_events(None, None)
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
@@ -363,21 +395,21 @@ def main():
     m_bytes = mla_bytes(m0.context_lens, m0.n_tokens, m0.head_num, max_blocks=m0.max_block_num)
     m_flops = mla_flops(m0.context_lens, None, m0.head_num, False)
 
+    # Per-call times come from events recorded on the calls' own kernels (start of
+    # the first, end of the last: mpaOperationSetLaunchEvents), so nothing but the
+    # kernels sits on the stream inside the timed region.
     def step(i, ev=None):
         if ev is not None:
-            ev[0].record()
+            p_op.set_launch_events(*ev[0])
+            m_ops[i % 2].set_launch_events(*ev[1])
         p_op.run()
-        if ev is not None:
-            ev[1].record()
         m_ops[i % 2].run()
-        if ev is not None:
-            ev[2].record()
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    evs = [launch_events(torch, 2) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     torch.cuda.synchronize()
     t_start.record()
@@ -386,8 +418,11 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    p_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
-    m_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    p_ms = float(np.mean([p[0].elapsed_time(p[1]) for p, _ in evs]))
+    m_ms = float(np.mean([m[0].elapsed_time(m[1]) for _, m in evs]))
+    p_op.set_launch_events(None, None)
+    for op in m_ops:
+        op.set_launch_events(None, None)
     p_tflops = p_flops / (p_ms * 1e-3) / 1e12
     m_gbs = m_bytes / (m_ms * 1e-3) / 1e9
     print(f"bench: prefill {p_ms:.4f} ms {p_tflops:.1f} TFLOP/s; decode {m_ms:.4f} ms {m_gbs:.0f} GB/s",
@@ -403,7 +438,7 @@ def main():
             op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
                                    mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
                                    q_start_loc=c.q_start_loc, return_lse=True)
-            ms = time_op(torch, op.run, 10, 3)
+            ms = time_ops(torch, [op], 10, 3)
             fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
             tf = fl / (ms * 1e-3) / 1e12
             e = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)}
@@ -414,7 +449,7 @@ def main():
             del c, op
             torch.cuda.empty_cache()
         # the same calls reading the page's compressed mask tile instead of generating
-        # the mask (register-staged kernel; one global read per 4 scores)
+        # the mask (one global read per 4 scores)
         for name, cfg in [("prefix_gqa_causal_norm_tile", None), ("alibi_right_4x4096_tile", "alibi_right_4x4096")]:
             print(f"bench: extra {name}", file=sys.stderr, flush=True)
             c = pc if cfg is None else W.make_prefill_config(cfg, device=dev)
@@ -423,7 +458,7 @@ def main():
             op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
                                    mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
                                    q_start_loc=c.q_start_loc, return_lse=True, compressed_mask=tile)
-            ms = time_op(torch, op.run, 10, 3)
+            ms = time_ops(torch, [op], 10, 3)
             fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
             extra[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                            "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
@@ -437,7 +472,7 @@ def main():
         op = mpa.PrefixEncoder(cc.query, cc.key, cc.value, cc.block_tables, cc.seq_len, cc.kv_seq_len,
                                mask_type=cc.mask_type, qk_scale=cc.qk_scale, return_lse=True,
                                attention_chunk=cc.chunk)
-        ms = time_op(torch, op.run, 10, 3)
+        ms = time_ops(torch, [op], 10, 3)
         fl = prefill_valid_flops_chunked(cc.seq_len, cc.kv_seq_len, cc.chunk, cc.head_num, cc.head_size)
         extra["chunked_16384_c2048"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                                         "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
@@ -448,7 +483,7 @@ def main():
         op4 = mpa.MLA(m4.q_nope, m4.q_rope, m4.ct_kv, m4.k_rope, m4.block_tables, m4.context_lens,
                       qk_scale=m4.qk_scale, q_seq_len=m4.q_seq_len, mask_type=m4.mask_type,
                       return_lse=True)
-        ms = time_op(torch, op4.run, 10, 3)
+        ms = time_ops(torch, [op4], 10, 3)
         fl = mla_flops(m4.context_lens, m4.q_seq_len, m4.head_num, True)
         by = mla_bytes(m4.context_lens, m4.n_tokens, m4.head_num, max_blocks=m4.max_block_num)
         extra["mla_spec_q4"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
@@ -463,7 +498,7 @@ def main():
         opp = mpa.MLA(mp.q_nope, mp.q_rope, mp.ct_kv, mp.k_rope, mp.block_tables, mp.context_lens,
                       qk_scale=mp.qk_scale, q_seq_len=mp.q_seq_len, mask_type=mp.mask_type,
                       calc_type=mp.calc_type, return_lse=True)
-        ms = time_op(torch, opp.run, 10, 3)
+        ms = time_ops(torch, [opp], 10, 3)
         fl = mla_flops(mp.context_lens, mp.q_seq_len, mp.head_num, True)
         extra["mla_prefill"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                                 "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
@@ -483,12 +518,7 @@ def main():
                         qk_scale=m.qk_scale, out=o8, lse=l8,
                         qk_descale=torch.as_tensor(m.qk_descale, device=dev),
                         pv_descale=torch.as_tensor(m.pv_descale, device=dev)) for m in m8]
-        flip = [0]
-
-        def run8():
-            ops8[flip[0]].run()
-            flip[0] ^= 1
-        ms = time_op(torch, run8, 20, 4)
+        ms = time_ops(torch, ops8, 20, 4)
         by = mla_bytes_int8(ctx8, m8[0].n_tokens, 128, max_blocks=64)
         fl = mla_flops(ctx8, None, 128, False)
         extra["mla_int8_decode_q1"] = {"ms": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),

@@ -284,6 +284,17 @@ mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void
 mpaStatus mpaLseMerge(const void *oParts, const float *lseParts, int32_t nParts, int64_t rows,
                       int32_t headDim, int dtype, void *out, float *lse, void *stream);
 
+/* Timing hooks, for callers that profile an operation's executions without
+ * adding commands to the stream between them.  startEvent / stopEvent are
+ * hipEvent_t handles created by the caller with timing enabled, or NULL (none).
+ * Each later execution of op records startEvent when its first kernel starts
+ * and stopEvent when its last kernel ends, on the kernels' own dispatch packets
+ * (hipExtLaunchKernel); an execution that launches nothing records neither.
+ * The events must stay valid while executions that record them are queued; the
+ * caller owns and destroys them.  Nothing is launched or allocated here.
+ * Errors: MPA_ERROR_INVALID_ARG if op is NULL. */
+mpaStatus mpaOperationSetLaunchEvents(mpaOperation *op, void *startEvent, void *stopEvent);
+
 /* Releases an operation (NULL is accepted).  Must not be called while an
  * execution of it may still be running on a stream. */
 mpaStatus mpaDestroyOperation(mpaOperation *op);

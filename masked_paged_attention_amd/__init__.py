@@ -72,6 +72,18 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _event(ev):
+    if ev is None:
+        return ctypes.c_void_p(0)
+    handle = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
+    _need(handle != 0, "the event has no HIP event yet: record it once before attaching it")
+    return ctypes.c_void_p(handle)
+
+
+def _set_launch_events(op, start, stop):
+    _check(LIB.mpaOperationSetLaunchEvents(op, _event(start), _event(stop)), "mpaOperationSetLaunchEvents")
+
+
 def _need(cond, msg):
     if not cond:
         raise ValueError(msg)
@@ -170,6 +182,11 @@ class PrefixEncoder:
                                                self._op, _stream(self.device, stream))
         _check(st, "mpaSelfAttentionPrefixEncoder")
         return (self.out, self.lse) if self.lse is not None else self.out
+
+    def set_launch_events(self, start=None, stop=None):
+        """Later runs record ``start`` / ``stop`` (torch.cuda.Event with timing, already
+        created by one record, or None) at their kernel's start and end."""
+        _set_launch_events(self._op, start, stop)
 
     def close(self):
         if getattr(self, "_op", None) is not None and self._op.value:
@@ -287,6 +304,11 @@ class MLA:
                         _stream(self.device, stream))
         _check(st, "mpaMLA")
         return (self.out, self.lse) if self.lse is not None else self.out
+
+    def set_launch_events(self, start=None, stop=None):
+        """Later runs record ``start`` at the split kernel's start and ``stop`` at the
+        end of the call's last kernel (torch.cuda.Event with timing, created, or None)."""
+        _set_launch_events(self._op, start, stop)
 
     def close(self):
         if getattr(self, "_op", None) is not None and self._op.value:

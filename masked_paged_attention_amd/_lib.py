@@ -57,6 +57,7 @@ SIGNATURES = {
     "mpaLseMerge": (ctypes.c_int32, [
         c_vp, c_vp, ctypes.c_int32, ctypes.c_int64,  # oParts, lseParts, nParts, rows
         ctypes.c_int32, ctypes.c_int, c_vp, c_vp, c_vp]),  # headDim, dtype, out, lse, stream
+    "mpaOperationSetLaunchEvents": (ctypes.c_int32, [c_vp, c_vp, c_vp]),
     "mpaDestroyOperation": (ctypes.c_int32, [c_vp]),
     "mpaGetErrorString": (ctypes.c_char_p, [ctypes.c_int32]),
     "mpaGetLastErrorMessage": (ctypes.c_char_p, []),

@@ -70,6 +70,7 @@ struct mpaOperation {
   // device copy of the plan
   void* dplan = nullptr;
   int device = 0;
+  mpa::LaunchEvents events{};  // timing hooks (mpaOperationSetLaunchEvents)
 
   ~mpaOperation() {
     if (dplan) {
@@ -185,6 +186,14 @@ const char* mpaGetErrorString(mpaStatus s) {
 }
 
 const char* mpaGetLastErrorMessage(void) { return g_last_error.c_str(); }
+
+mpaStatus mpaOperationSetLaunchEvents(mpaOperation* op, void* startEvent, void* stopEvent) {
+  g_last_error.clear();
+  if (!op) return fail(MPA_ERROR_INVALID_ARG, "op must not be NULL");
+  op->events.start = (hipEvent_t)startEvent;
+  op->events.stop = (hipEvent_t)stopEvent;
+  return MPA_OK;
+}
 
 mpaStatus mpaDestroyOperation(mpaOperation* op) {
   delete op;
@@ -330,7 +339,7 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize,
   if (!op || op->kind != mpaOperation::kPrefill)
     return fail(MPA_ERROR_INVALID_ARG, "op is not a PrefixEncoder operation");
   hipError_t e = mpa::launch_prefill(op->pp, op->dtype, op->head_size, op->mask_type, op->grid,
-                                     (hipStream_t)stream);
+                                     (hipStream_t)stream, op->events);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return MPA_OK;
 }
@@ -503,7 +512,7 @@ mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void
   mpa::MlaParams p = op->mp;
   p.part_o = (char*)workspace + op->part_o_off;
   p.part_lse = (float*)((char*)workspace + op->part_lse_off);
-  hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream);
+  hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream, op->events);
   if (e != hipSuccess) return hip_fail(e, "MLA launch");
   return MPA_OK;
 }

@@ -34,10 +34,17 @@ struct PrefillParams {
 constexpr int kMaskTileFlag = 16;
 constexpr int kMaskTile = 128;
 
+// Events a call records on its own kernels' dispatch packets (hipExtLaunchKernel):
+// start when its first kernel starts, stop when its last kernel ends; null = none.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // dtype: 0 fp16, 1 bf16; head_size 64/128; mask_type 0/3/4/5/9, 10 (chunked local
 // causal), or 3/4/5/9 | kMaskTileFlag (compressed tile in p.mask).
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
-                          int grid, hipStream_t stream);
+                          int grid, hipStream_t stream, const LaunchEvents& ev = {});
 
 struct MlaParams {
   const void* q_nope;          // [T, H, 512]
@@ -71,7 +78,7 @@ struct MlaParams {
   const float* pv_descale;     // [H] (quant only)
 };
 
-hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream);
+hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream, const LaunchEvents& ev = {});
 
 struct LseMergeParams {
   const void* o_parts;         // [n_parts, rows, head_dim] partial outputs

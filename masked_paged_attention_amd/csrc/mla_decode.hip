@@ -33,6 +33,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -724,33 +726,35 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
 }
 
 template <typename T, bool Q8>
-void launch_split(const MlaParams& p, hipStream_t s) {
+void launch_split(const MlaParams& p, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   if (p.bs_shift >= 5)
-    hipLaunchKernelGGL((mla_split_kernel<T, true, Q8>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
-                       p.segs, p.piece_seg, p.seqs, p.seqs2);
+    hipExtLaunchKernelGGL((mla_split_kernel<T, true, Q8>), dim3(p.grid), dim3(512), 0, s, start, stop, 0, p,
+                          p.block_tables, p.segs, p.piece_seg, p.seqs, p.seqs2);
   else
-    hipLaunchKernelGGL((mla_split_kernel<T, false, Q8>), dim3(p.grid), dim3(512), 0, s, p, p.block_tables,
-                       p.segs, p.piece_seg, p.seqs, p.seqs2);
+    hipExtLaunchKernelGGL((mla_split_kernel<T, false, Q8>), dim3(p.grid), dim3(512), 0, s, start, stop, 0, p,
+                          p.block_tables, p.segs, p.piece_seg, p.seqs, p.seqs2);
 }
 
 template <typename T>
-hipError_t launch_typed(const MlaParams& p, hipStream_t s) {
+hipError_t launch_typed(const MlaParams& p, hipStream_t s, const LaunchEvents& ev) {
+  // (the stop event goes on the combine when there is one)
+  hipEvent_t split_stop = p.any_parts ? nullptr : ev.stop;
   if (p.quant)
-    launch_split<T, true>(p, s);
+    launch_split<T, true>(p, s, ev.start, split_stop);
   else
-    launch_split<T, false>(p, s);
+    launch_split<T, false>(p, s, ev.start, split_stop);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.any_parts) return e;
-  hipLaunchKernelGGL(mla_combine_kernel<T>, dim3((p.max_rows + 3) / 4, p.batch), dim3(256), 0, s, p,
-                     p.seqs, p.seqs2);
+  hipExtLaunchKernelGGL(mla_combine_kernel<T>, dim3((p.max_rows + 3) / 4, p.batch), dim3(256), 0, s,
+                        nullptr, ev.stop, 0, p, p.seqs, p.seqs2);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_mla(const MlaParams& p, int dtype, hipStream_t stream, const LaunchEvents& ev) {
   if (p.grid <= 0) return hipSuccess;
-  return dtype == 0 ? launch_typed<_Float16>(p, stream) : launch_typed<__bf16>(p, stream);
+  return dtype == 0 ? launch_typed<_Float16>(p, stream, ev) : launch_typed<__bf16>(p, stream, ev);
 }
 
 }  // namespace mpa

@@ -38,6 +38,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -866,43 +868,43 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 }
 
 template <typename T, int D>
-hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s) {
+hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s, const LaunchEvents& ev) {
   const dim3 g(grid), blk(256);
   if (D == 128 && p.bs_shift >= 6) {
     switch (mask_type) {
       case kMaskTileFlag | 3:
-        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 3>), g, blk, 0, s, p, p.block_tables);
+        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 3>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;
       case kMaskTileFlag | 4:
-        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 4>), g, blk, 0, s, p, p.block_tables);
+        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 4>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;
       case kMaskTileFlag | 5:
-        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 5>), g, blk, 0, s, p, p.block_tables);
+        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 5>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;
       case kMaskTileFlag | 9:
-        hipLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 9>), g, blk, 0, s, p, p.block_tables);
+        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 9>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;
-      case 0: hipLaunchKernelGGL((prefill_dma_kernel<T, 0>), g, blk, 0, s, p, p.block_tables); break;
-      case 3: hipLaunchKernelGGL((prefill_dma_kernel<T, 3>), g, blk, 0, s, p, p.block_tables); break;
-      case 4: hipLaunchKernelGGL((prefill_dma_kernel<T, 4>), g, blk, 0, s, p, p.block_tables); break;
-      case 5: hipLaunchKernelGGL((prefill_dma_kernel<T, 5>), g, blk, 0, s, p, p.block_tables); break;
-      case 9: hipLaunchKernelGGL((prefill_dma_kernel<T, 9>), g, blk, 0, s, p, p.block_tables); break;
-      case 10: hipLaunchKernelGGL((prefill_dma_kernel<T, 10>), g, blk, 0, s, p, p.block_tables); break;
+      case 0: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 0>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
+      case 3: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 3>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
+      case 4: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 4>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
+      case 5: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 5>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
+      case 9: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 9>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
+      case 10: hipExtLaunchKernelGGL((prefill_dma_kernel<T, 10>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (mask_type) {
-    case 0: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 0>), g, blk, 0, s, p); break;
-    case 3: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 3>), g, blk, 0, s, p); break;
-    case 4: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 4>), g, blk, 0, s, p); break;
-    case 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 5>), g, blk, 0, s, p); break;
-    case 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 9>), g, blk, 0, s, p); break;
-    case 10: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, 10>), g, blk, 0, s, p); break;
-    case kMaskTileFlag | 3: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 3>), g, blk, 0, s, p); break;
-    case kMaskTileFlag | 4: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 4>), g, blk, 0, s, p); break;
-    case kMaskTileFlag | 5: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 5>), g, blk, 0, s, p); break;
-    case kMaskTileFlag | 9: hipLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 9>), g, blk, 0, s, p); break;
+    case 0: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 0>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case 3: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 3>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case 4: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 4>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case 5: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 5>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case 9: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 9>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case 10: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, 10>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case kMaskTileFlag | 3: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 3>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case kMaskTileFlag | 4: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 4>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case kMaskTileFlag | 5: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 5>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
+    case kMaskTileFlag | 9: hipExtLaunchKernelGGL((prefill_fwd_kernel<T, D, kMaskTileFlag | 9>), g, blk, 0, s, ev.start, ev.stop, 0, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -911,14 +913,14 @@ hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStrea
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int head_size, int mask_type,
-                          int grid, hipStream_t stream) {
+                          int grid, hipStream_t stream, const LaunchEvents& ev) {
   if (grid <= 0) return hipSuccess;
   if (dtype == 0) {
-    return head_size == 64 ? launch_mask<_Float16, 64>(p, mask_type, grid, stream)
-                           : launch_mask<_Float16, 128>(p, mask_type, grid, stream);
+    return head_size == 64 ? launch_mask<_Float16, 64>(p, mask_type, grid, stream, ev)
+                           : launch_mask<_Float16, 128>(p, mask_type, grid, stream, ev);
   }
-  return head_size == 64 ? launch_mask<__bf16, 64>(p, mask_type, grid, stream)
-                         : launch_mask<__bf16, 128>(p, mask_type, grid, stream);
+  return head_size == 64 ? launch_mask<__bf16, 64>(p, mask_type, grid, stream, ev)
+                         : launch_mask<__bf16, 128>(p, mask_type, grid, stream, ev);
 }
 
 }  // namespace mpa

@@ -179,6 +179,10 @@ def test_mla_execute_rejects_small_workspace_and_wrong_op(lib):
     assert lib.mpaSelfAttentionPrefixEncoder(None, 0, None, None) == 1
 
 
+def test_launch_events_need_an_operation(lib):
+    assert lib.mpaOperationSetLaunchEvents(None, None, None) == 1
+
+
 # ---------------------------------------------------------------------------
 # Planners (host only).
 # ---------------------------------------------------------------------------

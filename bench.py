@@ -218,6 +218,27 @@ def summarize_traffic(fetch_csv, write_csv, command, copy_bytes=1 << 30):
     return "\n".join(out) + "\n"
 
 
+def summarize_counters(pmc_csv, command):
+    """Per-kernel means over dispatches of every counter in a rocprofv3 --pmc
+    counter_collection.csv (device copies left out)."""
+    vals = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        if "copyBuffer" in r["Kernel_Name"]:
+            continue
+        key = (short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+        vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    counters = sorted({c for _, c in vals})
+    kernels = sorted({k for k, _ in vals})
+    out = ["# rocprofv3 hardware counters, mean per dispatch", "# command:", "#   " + command,
+           f"# kernel sources digest: {kernel_source_digest()}", "",
+           f"{'kernel':40s} {'dispatches':>10s} " + " ".join(f"{c:>16s}" for c in counters)]
+    for k in kernels:
+        n = max(len(vals.get((k, c), [])) for c in counters)
+        out.append(f"{k:40s} {n:10d} " + " ".join(
+            f"{float(np.mean(vals[(k, c)])):16.4g}" if (k, c) in vals else f"{'-':>16s}" for c in counters))
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(kernel_prefix, path=TRAFFIC_SUMMARY):
     """HBM bytes per dispatch of the first kernel whose short name starts with
     kernel_prefix, from the committed counter summary; None when the summary is
@@ -339,6 +360,8 @@ def main():
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print HBM bytes per dispatch from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
+                    help="print per-kernel means of a rocprofv3 --pmc counter_collection.csv and exit")
     ap.add_argument("--command", default="", help="the profiling command(s), recorded in a summary")
     args = ap.parse_args()
     if args.summarize_stats:
@@ -346,6 +369,9 @@ def main():
         return
     if args.summarize_traffic:
         sys.stdout.write(summarize_traffic(*args.summarize_traffic, args.command))
+        return
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters, args.command))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "

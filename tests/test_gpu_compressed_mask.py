@@ -27,6 +27,9 @@ CASES = [
     ([300, 1, 0, 129], [700, 128, 5, 129], 8, 2, 128, 128),
     ([200, 77], [457, 333], 4, 4, 64, 16),
     ([256, 40], [256, 300], 4, 1, 128, 24),
+    # headSize 128 with 64- and 256-key cache blocks (the direct-load kernel)
+    ([257, 64, 3], [513, 64, 200], 8, 2, 128, 64),
+    ([130, 500], [700, 500], 4, 4, 128, 256),
 ]
 
 

@@ -84,7 +84,8 @@ def test_row_hidden_by_the_tile_is_zero():
     assert np.all(np.isneginf(rl[5]))
 
 
-@pytest.mark.parametrize("name", ["prefix_gqa_causal", "alibi_right_4x4096"])
+@pytest.mark.parametrize("name", ["prefix_gqa_causal", "alibi_right_4x4096", "alibi_sqrt_16384",
+                                  "alibi_left_16384"])
 def test_compressed_mask_full_size_sampled(name):
     # the bench's compressed-tile calls: the full workloads with the page's tile
     log(f"case compressed full-size {name} (sampled rows)")

@@ -24,9 +24,12 @@
  *   - "dev" pointers are HIP device pointers, "HOST" pointers are ordinary host
  *     memory read during the call that receives them (the host arrays are copied
  *     into the operation, so the caller may free them afterwards);
- *   - the caller owns every tensor and the workspace; the library owns only the
- *     mpaOperation (host object plus a small device copy of its launch plan),
- *     released by mpaDestroyOperation;
+ *   - the caller owns every tensor and the workspace, and the library allocates
+ *     no device memory: it owns only the mpaOperation (a host object and its
+ *     launch plan, kept in pinned host memory), released by mpaDestroyOperation.
+ *     Every execution first copies the plan into the head of the workspace
+ *     (one asynchronous host-to-device copy on the execution's stream), then
+ *     launches the kernels, which read the plan there;
  *   - all shape and argument checks happen in the first phase, on the host,
  *     before any HIP call; on error *op is set to NULL and a status != MPA_OK is
  *     returned; mpaGetLastErrorMessage() then describes the failure (per thread);
@@ -107,8 +110,9 @@ typedef struct mpaOperation mpaOperation; /* opaque, library-owned */
  *   nTokens      rows of query and attnOut (>= every qStartLoc[b] + seqLen[b])
  *   attnOut      dev  [nTokens, headNum, headSize] dtype (output)
  *   lse          dev  [nTokens, headNum] fp32 natural-log LSE (output), or NULL
- *   workspaceSize, op  outputs: bytes of device workspace phase 2 needs (0 for
- *                this operation) and the new operation
+ *   workspaceSize, op  outputs: bytes of device workspace phase 2 needs (the
+ *                launch plan: 16 bytes per workgroup plus 16 per sequence, each
+ *                part rounded up to 256 bytes) and the new operation
  */
 mpaStatus mpaSelfAttentionPrefixEncoderGetWorkspaceSize(
     const void *query, const void *key, const void *value, const int32_t *blockTables,
@@ -175,8 +179,11 @@ mpaStatus mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
     int32_t maxBlockNum, int dtype, const int64_t *qStartLoc, int64_t nTokens, void *attnOut,
     float *lse, uint64_t *workspaceSize, mpaOperation **op);
 
-/* PrefixEncoder, phase 2: launch on `stream` (hipStream_t).  `workspace` may be
- * NULL when the size phase 1 returned is 0. */
+/* PrefixEncoder, phase 2: copy of the plan into `workspace` (dev, >= the size
+ * phase 1 returned, 256-byte aligned) and one kernel launch, both on `stream`
+ * (hipStream_t).  Errors: MPA_ERROR_INVALID_ARG for a NULL or misaligned
+ * workspace or another kind of operation, MPA_ERROR_WORKSPACE_TOO_SMALL,
+ * MPA_ERROR_HIP if the copy or the launch fails. */
 mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
                                         mpaOperation *op, void *stream);
 
@@ -216,17 +223,20 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
  *              MPA_ERROR_UNSUPPORTED; the int8 cache is served on the ND layout by
  *              mpaMLAInt8GetWorkspaceSize, RING's single-GPU part by mpaLseMerge)
  *   batch, numBlocks, blockSize, maxBlockNum, dtype   as for PrefixEncoder
+ *   nTokens    T, the query tokens: batch for calcType UNDEFINED, the sum of
+ *              qSeqLen otherwise (anything else is MPA_ERROR_INVALID_ARG)
  *   attenOut   dev [T, headNum, 512] dtype (output)
  *   lse        dev [T, headNum] fp32 natural-log LSE (output), or NULL
- *   workspaceSize, op  outputs: device workspace bytes (split-KV partial
- *              results) and the new operation
+ *   workspaceSize, op  outputs: device workspace bytes (the launch plan, then
+ *              the split-KV partial results) and the new operation
  */
 mpaStatus mpaMLAGetWorkspaceSize(
     const void *qNope, const void *qRope, const void *ctKV, const void *kRope,
     const int32_t *blockTables, const int32_t *contextLens, const int32_t *qSeqLen,
     int32_t headNum, float qkScale, int32_t kvHeadNum, int maskType, int calcType,
     int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize, int32_t maxBlockNum,
-    int dtype, void *attenOut, float *lse, uint64_t *workspaceSize, mpaOperation **op);
+    int dtype, int64_t nTokens, void *attenOut, float *lse, uint64_t *workspaceSize,
+    mpaOperation **op);
 
 /*
  * MLA, phase 1, over an int8 latent cache (ATB page "MLA", parameter table:
@@ -250,12 +260,13 @@ mpaStatus mpaMLAInt8GetWorkspaceSize(
     const int32_t *blockTables, const int32_t *contextLens, const int32_t *qSeqLen,
     const float *qkDescale, const float *pvDescale, int32_t headNum, float qkScale,
     int32_t kvHeadNum, int maskType, int calcType, int32_t batch, int32_t numBlocks,
-    int32_t blockSize, int32_t maxBlockNum, int dtype, void *attenOut, float *lse,
-    uint64_t *workspaceSize, mpaOperation **op);
+    int32_t blockSize, int32_t maxBlockNum, int dtype, int64_t nTokens, void *attenOut,
+    float *lse, uint64_t *workspaceSize, mpaOperation **op);
 
-/* MLA, phase 2: two launches on `stream` -- split-KV partials into the
- * workspace (>= the size phase 1 returned, 256-byte aligned), then their
- * LSE-weighted merge into attenOut / lse. */
+/* MLA, phase 2, on `stream`: copy of the plan into the workspace (dev, >= the
+ * size phase 1 returned, 256-byte aligned), the split kernel (partials into the
+ * workspace) and, when a sequence was split, their LSE-weighted merge into
+ * attenOut / lse.  Errors as for mpaSelfAttentionPrefixEncoder. */
 mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void *stream);
 
 /*
@@ -266,8 +277,9 @@ mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void
  * chunks of a long prefix, or one GPU's range of a ring.  For row r and part s:
  *   LSE_r = ln sum_s exp(lseParts[s][r]),
  *   out[r] = sum_s exp(lseParts[s][r] - LSE_r) * oParts[s][r].
- * A part with LSE = -inf (no key in its range) weighs nothing; a row whose
- * parts are all -inf gets out = 0 and LSE = -inf.  One launch on `stream`;
+ * A part with LSE = -inf (no key in its range) weighs nothing and its output
+ * values are ignored (they may be undefined, NaN included); a row whose parts
+ * are all -inf gets out = 0 and LSE = -inf.  One launch on `stream`;
  * nothing is allocated.
  *   oParts    dev [nParts, rows, headDim] dtype, contiguous (parts stacked)
  *   lseParts  dev [nParts, rows] fp32, natural log (as written by the lse
@@ -309,15 +321,17 @@ const char *mpaGetLastErrorMessage(void);
  * Host-only inspection of the PrefixEncoder launch plan (no HIP call; for tests
  * and tools).  Fills items[0 .. *nItems) with 4 int32 each, one per workgroup in
  * launch order: {b, first query head, first query row, number of key tiles the
- * workgroup visits}, and reports the tile geometry.  Returns
- * MPA_ERROR_INVALID_ARG if capacity (in items) is too small; *nItems is set
- * either way.
+ * workgroup visits}, and reports the tile geometry and the workspace bytes
+ * phase 1 would return for the plan (any output pointer may be NULL).  Returns
+ * MPA_ERROR_INVALID_ARG if capacity (in items) is too small; *nItems and the
+ * scalar outputs are set either way.
  */
 mpaStatus mpaPrefixEncoderPlanInspect(const int32_t *seqLen, const int32_t *kvSeqLen,
                                       int32_t batch, int maskType, int32_t headNum,
                                       int32_t kvHeadNum, int32_t headSize, int32_t *items,
                                       int64_t capacity, int64_t *nItems, int32_t *rowsPerItem,
-                                      int32_t *keysPerTile, int32_t *headsPerItem);
+                                      int32_t *keysPerTile, int32_t *headsPerItem,
+                                      uint64_t *workspaceSize);
 
 /*
  * Host-only inspection of the MLA split plan (as planned for 256 compute

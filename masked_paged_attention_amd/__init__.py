@@ -261,12 +261,16 @@ class MLA:
         T, H, _ = q_nope.shape
         self._ctx, p_ctx = _host_i32(context_lens)
         B = len(self._ctx)
+        _need(block_tables.shape[0] == B, "block_tables needs one row per sequence")
         if calc_type is None:
             calc_type = MLA_CALC_UNDEFINED if q_seq_len is None else MLA_CALC_SPEC
         if q_seq_len is not None:
             self._ql, p_ql = _host_i32(q_seq_len)
+            _need(len(self._ql) == B, "q_seq_len needs one entry per sequence")
+            _need(T == int(self._ql.astype(np.int64).sum()), "q_nope has sum(q_seq_len) token rows")
         else:
             self._ql, p_ql = None, ctypes.POINTER(ctypes.c_int32)()
+            _need(T == B, "q_nope has one token row per sequence")
         self.out = out if out is not None else torch.empty(q_nope.shape, dtype=dt, device=q_nope.device)
         _need(self.out.shape == q_nope.shape and self.out.dtype == dt and self.out.is_contiguous(),
               "out must be [T, H, 512] of the input dtype")
@@ -284,14 +288,14 @@ class MLA:
             st = LIB.mpaMLAInt8GetWorkspaceSize(
                 _ptr(q_nope), _ptr(q_rope), _ptr(ct_kv), _ptr(k_rope), _ptr(block_tables), p_ctx, p_ql,
                 _ptr(qk_descale), _ptr(pv_descale), H, float(qk_scale), 1, int(mask_type), int(calc_type),
-                B, ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], _ptr(self.out),
+                B, ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], T, _ptr(self.out),
                 _ptr(lse), ctypes.byref(ws), ctypes.byref(op))
             _check(st, "mpaMLAInt8GetWorkspaceSize")
         else:
             st = LIB.mpaMLAGetWorkspaceSize(
                 _ptr(q_nope), _ptr(q_rope), _ptr(ct_kv), _ptr(k_rope), _ptr(block_tables), p_ctx, p_ql,
                 H, float(qk_scale), 1, int(mask_type), int(calc_type), int(cache_mode), B,
-                ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], _ptr(self.out),
+                ct_kv.shape[0], ct_kv.shape[1], block_tables.shape[1], _DTYPES[dt], T, _ptr(self.out),
                 _ptr(lse), ctypes.byref(ws), ctypes.byref(op))
             _check(st, "mpaMLAGetWorkspaceSize")
         self._op = op
@@ -365,23 +369,28 @@ def lse_merge(o_parts, lse_parts, *, out=None, lse=None, return_lse=True, stream
     return (out, lse) if lse is not None else out
 
 
-def plan_prefill(seq_len, kv_seq_len, mask_type, head_num, kv_head_num, head_size=128):
+def plan_prefill(seq_len, kv_seq_len, mask_type, head_num, kv_head_num, head_size=128,
+                 with_workspace=False):
     """Host-only view of the prefill launch plan: (items [n, 4] int32 {b, head0, row0,
-    n_tiles}, rows_per_item, keys_per_tile, heads_per_item)."""
+    n_tiles}, rows_per_item, keys_per_tile, heads_per_item), plus the workspace
+    bytes phase 1 returns for it with ``with_workspace``."""
     s, ps = _host_i32(seq_len)
     k, pk = _host_i32(kv_seq_len)
     n = ctypes.c_int64(0)
     rows, keys, heads = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    ws = ctypes.c_uint64(0)
     LIB.mpaPrefixEncoderPlanInspect(ps, pk, len(s), int(mask_type), head_num, kv_head_num, head_size,
                                     ctypes.POINTER(ctypes.c_int32)(), 0, ctypes.byref(n),
-                                    ctypes.byref(rows), ctypes.byref(keys), ctypes.byref(heads))
+                                    ctypes.byref(rows), ctypes.byref(keys), ctypes.byref(heads),
+                                    ctypes.byref(ws))
     items = np.zeros((max(1, n.value), 4), dtype=np.int32)
     st = LIB.mpaPrefixEncoderPlanInspect(ps, pk, len(s), int(mask_type), head_num, kv_head_num,
                                          head_size, items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                          n.value, ctypes.byref(n), ctypes.byref(rows),
-                                         ctypes.byref(keys), ctypes.byref(heads))
+                                         ctypes.byref(keys), ctypes.byref(heads), ctypes.byref(ws))
     _check(st, "mpaPrefixEncoderPlanInspect")
-    return items[:n.value], rows.value, keys.value, heads.value
+    res = (items[:n.value], rows.value, keys.value, heads.value)
+    return res + (ws.value,) if with_workspace else res
 
 
 def plan_mla(context_lens, q_seq_len, head_num, calc_type):

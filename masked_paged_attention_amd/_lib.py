@@ -45,14 +45,16 @@ SIGNATURES = {
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32,  # headNum, qkScale, kvHeadNum
         ctypes.c_int, ctypes.c_int, ctypes.c_int,    # maskType, calcType, cacheMode
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, numBlocks, blockSize, maxBlockNum
-        ctypes.c_int, c_vp, c_vp, c_u64p, c_opp]),   # dtype, attenOut, lse, workspaceSize, op
+        ctypes.c_int, ctypes.c_int64,                # dtype, nTokens
+        c_vp, c_vp, c_u64p, c_opp]),                 # attenOut, lse, workspaceSize, op
     "mpaMLAInt8GetWorkspaceSize": (ctypes.c_int32, [
         c_vp, c_vp, c_vp, c_vp, c_vp,                # qNope, qRope, ctKV, kRope, blockTables
         c_i32p, c_i32p, c_vp, c_vp,                  # contextLens, qSeqLen, qkDescale, pvDescale
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32,  # headNum, qkScale, kvHeadNum
         ctypes.c_int, ctypes.c_int,                  # maskType, calcType
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,  # batch, numBlocks, blockSize, maxBlockNum
-        ctypes.c_int, c_vp, c_vp, c_u64p, c_opp]),   # dtype, attenOut, lse, workspaceSize, op
+        ctypes.c_int, ctypes.c_int64,                # dtype, nTokens
+        c_vp, c_vp, c_u64p, c_opp]),                 # attenOut, lse, workspaceSize, op
     "mpaMLA": (ctypes.c_int32, [c_vp, ctypes.c_uint64, c_vp, c_vp]),
     "mpaLseMerge": (ctypes.c_int32, [
         c_vp, c_vp, ctypes.c_int32, ctypes.c_int64,  # oParts, lseParts, nParts, rows
@@ -63,7 +65,7 @@ SIGNATURES = {
     "mpaGetLastErrorMessage": (ctypes.c_char_p, []),
     "mpaPrefixEncoderPlanInspect": (ctypes.c_int32, [
         c_i32p, c_i32p, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32, c_i32p, ctypes.c_int64, c_i64p, c_i32p, c_i32p, c_i32p]),
+        ctypes.c_int32, c_i32p, ctypes.c_int64, c_i64p, c_i32p, c_i32p, c_i32p, c_u64p]),
     "mpaMLAPlanInspect": (ctypes.c_int32, [
         c_i32p, c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, c_i32p, ctypes.c_int64,
         c_i64p]),

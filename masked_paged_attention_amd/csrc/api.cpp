@@ -3,9 +3,11 @@
 //
 // Phase 1 (…GetWorkspaceSize) validates every argument on the host first --
 // nothing touches HIP until all checks pass -- then plans the launch on the host
-// and uploads the plan once into a small device buffer owned by the operation.
-// Phase 2 is then a pure launch (no copy, no allocation): one kernel for the
-// prefix encoder, split + combine for MLA.
+// and keeps the plan in pinned host memory owned by the operation; the
+// workspace size it reports covers the plan (and, for MLA, the split-KV
+// partials).  Phase 2 copies the plan into the head of the caller's workspace
+// with one asynchronous copy on the caller's stream and launches the kernels
+// there: the library allocates no device memory.
 
 #include <hip/hip_runtime.h>
 
@@ -65,48 +67,74 @@ struct mpaOperation {
   int grid = 0;
   // mla
   mpa::MlaParams mp{};
-  uint64_t ws_bytes = 0;
   uint64_t part_o_off = 0, part_lse_off = 0;
-  // device copy of the plan
-  void* dplan = nullptr;
-  int device = 0;
+  // launch plan: pinned host copy, copied to workspace[0, plan_bytes) by every
+  // execution; blob i sits at plan_offs[i]
+  void* hplan = nullptr;
+  uint64_t plan_bytes = 0;
+  std::vector<size_t> plan_offs;
+  uint64_t ws_bytes = 0;       // workspace bytes an execution needs
   mpa::LaunchEvents events{};  // timing hooks (mpaOperationSetLaunchEvents)
 
   ~mpaOperation() {
-    if (dplan) {
-      int cur = 0;
-      if (hipGetDevice(&cur) == hipSuccess && cur != device) {
-        (void)hipSetDevice(device);
-        (void)hipFree(dplan);
-        (void)hipSetDevice(cur);
-      } else {
-        (void)hipFree(dplan);
-      }
-    }
+    if (hplan) (void)hipHostFree(hplan);
   }
 };
 
 namespace {
 
-// Copies a host plan (a list of byte blobs, each 16-byte aligned) to the device
-// in one allocation; returns the device base and the blob offsets.
-mpaStatus upload(mpaOperation* op, const std::vector<std::pair<const void*, size_t>>& blobs,
-                 std::vector<size_t>& offs) {
-  size_t total = 0;
+constexpr uint64_t kWsAlign = 256;
+uint64_t align_up(uint64_t x) { return (x + kWsAlign - 1) & ~(kWsAlign - 1); }
+
+// Byte offsets of plan blobs laid out one after another, each 256-byte aligned;
+// returns the total.
+uint64_t plan_layout(const std::vector<size_t>& sizes, std::vector<size_t>& offs) {
+  uint64_t total = 0;
   offs.clear();
-  for (auto& bl : blobs) {
+  for (size_t n : sizes) {
     offs.push_back(total);
-    total += (bl.second + 255) & ~size_t(255);
+    total += align_up(n);
   }
-  std::vector<char> host(total ? total : 16, 0);
+  return total;
+}
+
+// Workspace bytes of a prefill plan of n_items work items over `batch` sequences
+// (the items, then one 16-byte record per sequence).
+uint64_t prefill_plan_bytes(size_t n_items, int batch) {
+  std::vector<size_t> offs;
+  return plan_layout({n_items * sizeof(mpa::PrefillItem), (size_t)batch * 4 * sizeof(int32_t)}, offs);
+}
+
+// Copies a host plan (a list of byte blobs) into pinned host memory owned by the
+// operation, in the layout of plan_layout.
+mpaStatus stage_plan(mpaOperation* op, const std::vector<std::pair<const void*, size_t>>& blobs) {
+  std::vector<size_t> sizes;
+  for (auto& bl : blobs) sizes.push_back(bl.second);
+  op->plan_bytes = plan_layout(sizes, op->plan_offs);
+  const size_t alloc = op->plan_bytes ? op->plan_bytes : kWsAlign;
+  hipError_t e = hipHostMalloc(&op->hplan, alloc, hipHostMallocDefault);
+  if (e != hipSuccess) {
+    op->hplan = nullptr;
+    return hip_fail(e, "hipHostMalloc (operation plan)");
+  }
+  std::memset(op->hplan, 0, alloc);
   for (size_t i = 0; i < blobs.size(); ++i)
-    if (blobs[i].second) std::memcpy(host.data() + offs[i], blobs[i].first, blobs[i].second);
-  hipError_t e = hipGetDevice(&op->device);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  e = hipMalloc(&op->dplan, host.size());
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc (operation plan)");
-  e = hipMemcpy(op->dplan, host.data(), host.size(), hipMemcpyHostToDevice);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (operation plan)");
+    if (blobs[i].second) std::memcpy((char*)op->hplan + op->plan_offs[i], blobs[i].first, blobs[i].second);
+  return MPA_OK;
+}
+
+// Checks the caller's workspace and queues the copy of the plan into its head.
+mpaStatus bind_workspace(const mpaOperation* op, void* workspace, uint64_t workspaceSize, hipStream_t stream) {
+  if (workspaceSize < op->ws_bytes)
+    return fail(MPA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes, %llu needed",
+                (unsigned long long)workspaceSize, (unsigned long long)op->ws_bytes);
+  if (op->ws_bytes && !workspace) return fail(MPA_ERROR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace) & (kWsAlign - 1))
+    return fail(MPA_ERROR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (op->plan_bytes) {
+    hipError_t e = hipMemcpyAsync(workspace, op->hplan, op->plan_bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan to workspace)");
+  }
   return MPA_OK;
 }
 
@@ -231,14 +259,13 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
   o->head_size = headSize;
   o->mask_type = chunk > 0 ? kMaskChunkedCausal : mask ? (maskType | mpa::kMaskTileFlag) : maskType;
   o->grid = (int)plan.items.size();
-  std::vector<size_t> offs;
-  st = upload(o, {{plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem)},
-                  {seqs.data(), seqs.size() * sizeof(int32_t)}},
-              offs);
+  st = stage_plan(o, {{plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem)},
+                      {seqs.data(), seqs.size() * sizeof(int32_t)}});
   if (st != MPA_OK) {
     delete o;
     return st;
   }
+  o->ws_bytes = o->plan_bytes;
   mpa::PrefillParams& p = o->pp;
   p.q = query;
   p.k = key;
@@ -247,8 +274,8 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
   p.lse = lse;
   p.block_tables = blockTables;
   p.slopes = slopes;
-  p.items = (const int4*)((char*)o->dplan + offs[0]);
-  p.seqs = (const int4*)((char*)o->dplan + offs[1]);
+  p.items = nullptr;  // in the workspace (bound at execution)
+  p.seqs = nullptr;
   p.head_num = headNum;
   p.kv_head_num = kvHeadNum;
   p.block_size = blockSize;
@@ -259,7 +286,7 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
   p.mask = mask;
   p.mask_stride = maskStride;
   p.scale2 = qkScale * kLog2e;
-  *workspaceSize = 0;
+  *workspaceSize = o->ws_bytes;
   *op = o;
   return MPA_OK;
 }
@@ -333,12 +360,15 @@ mpaStatus mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
 
 mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize, mpaOperation* op,
                                         void* stream) {
-  (void)workspace;
-  (void)workspaceSize;
   g_last_error.clear();
   if (!op || op->kind != mpaOperation::kPrefill)
     return fail(MPA_ERROR_INVALID_ARG, "op is not a PrefixEncoder operation");
-  hipError_t e = mpa::launch_prefill(op->pp, op->dtype, op->head_size, op->mask_type, op->grid,
+  mpaStatus st = bind_workspace(op, workspace, workspaceSize, (hipStream_t)stream);
+  if (st != MPA_OK) return st;
+  mpa::PrefillParams p = op->pp;
+  p.items = (const int4*)((char*)workspace + op->plan_offs[0]);
+  p.seqs = (const int4*)((char*)workspace + op->plan_offs[1]);
+  hipError_t e = mpa::launch_prefill(p, op->dtype, op->head_size, op->mask_type, op->grid,
                                      (hipStream_t)stream, op->events);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return MPA_OK;
@@ -352,7 +382,7 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
                       const int32_t* blockTables, const int32_t* contextLens, const int32_t* qSeqLen,
                       int32_t headNum, float qkScale, int32_t kvHeadNum, int maskType, int calcType,
                       int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
-                      int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
+                      int32_t maxBlockNum, int dtype, int64_t nTokens, void* attenOut, float* lse,
                       uint64_t* workspaceSize, mpaOperation** op, bool quant, const float* qkDescale,
                       const float* pvDescale) {
   if (!op || !workspaceSize) return fail(MPA_ERROR_INVALID_ARG, "workspaceSize and op must not be NULL");
@@ -388,8 +418,10 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   if (numBlocks < 1 || blockSize < 1 || maxBlockNum < 1)
     return fail(MPA_ERROR_INVALID_ARG, "numBlocks, blockSize and maxBlockNum must be >= 1");
   std::vector<int32_t> qlen(batch, 1);
+  int64_t tokens = 0;
   for (int b = 0; b < batch; ++b) {
     if (qSeqLen) qlen[b] = qSeqLen[b];
+    tokens += qlen[b] > 0 ? qlen[b] : 0;
     if (contextLens[b] < 1) return fail(MPA_ERROR_INVALID_ARG, "sequence %d: contextLens must be >= 1", b);
     if (qlen[b] < 1 || qlen[b] > contextLens[b])
       return fail(MPA_ERROR_INVALID_ARG, "sequence %d: need 1 <= qSeqLen (%d) <= contextLens (%d)", b,
@@ -398,6 +430,10 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
       return fail(MPA_ERROR_INVALID_ARG, "sequence %d: contextLens %d needs more than maxBlockNum=%d blocks",
                   b, contextLens[b], maxBlockNum);
   }
+  if (nTokens != tokens)
+    return fail(MPA_ERROR_INVALID_ARG,
+                "nTokens (%lld) must equal the query tokens of the batch (%lld: %s)", (long long)nTokens,
+                (long long)tokens, many_tokens ? "the sum of qSeqLen" : "one per sequence");
 
   int dev = 0, cus = 256;
   hipError_t e = hipGetDevice(&dev);
@@ -423,12 +459,10 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   if (!o) return fail(MPA_ERROR_HIP, "out of host memory");
   o->kind = mpaOperation::kMla;
   o->dtype = dtype;
-  std::vector<size_t> offs;
-  mpaStatus st = upload(o, {{plan.segs.data(), plan.segs.size() * sizeof(mpa::MlaSegment)},
-                            {plan.piece_seg.data(), plan.piece_seg.size() * 4},
-                            {seqs.data(), seqs.size() * 4},
-                            {seqs2.data(), seqs2.size() * 4}},
-                        offs);
+  mpaStatus st = stage_plan(o, {{plan.segs.data(), plan.segs.size() * sizeof(mpa::MlaSegment)},
+                                {plan.piece_seg.data(), plan.piece_seg.size() * 4},
+                                {seqs.data(), seqs.size() * 4},
+                                {seqs2.data(), seqs2.size() * 4}});
   if (st != MPA_OK) {
     delete o;
     return st;
@@ -439,10 +473,10 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   p.ckv = ctKV;
   p.krope = kRope;
   p.block_tables = blockTables;
-  p.segs = (const int4*)((char*)o->dplan + offs[0]);
-  p.piece_seg = (const int32_t*)((char*)o->dplan + offs[1]);
-  p.seqs = (const int4*)((char*)o->dplan + offs[2]);
-  p.seqs2 = (const int4*)((char*)o->dplan + offs[3]);
+  p.segs = nullptr;  // plan and partials live in the workspace (bound at execution)
+  p.piece_seg = nullptr;
+  p.seqs = nullptr;
+  p.seqs2 = nullptr;
   p.out = attenOut;
   p.lse = lse;
   p.head_num = headNum;
@@ -461,9 +495,10 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   p.quant = quant ? 1 : 0;
   p.qk_descale = qkDescale;
   p.pv_descale = pvDescale;
-  o->part_o_off = 0;
-  o->part_lse_off = ((uint64_t)plan.part_rows * 512 * 2 + 255) & ~uint64_t(255);
-  o->ws_bytes = o->part_lse_off + (((uint64_t)plan.part_rows * 4 + 255) & ~uint64_t(255));
+  // workspace: plan, partial outputs (input type), partial LSEs (fp32)
+  o->part_o_off = o->plan_bytes;
+  o->part_lse_off = o->part_o_off + align_up((uint64_t)plan.part_rows * 512 * 2);
+  o->ws_bytes = o->part_lse_off + align_up((uint64_t)plan.part_rows * 4);
   *workspaceSize = o->ws_bytes;
   *op = o;
   return MPA_OK;
@@ -476,13 +511,13 @@ mpaStatus mpaMLAGetWorkspaceSize(const void* qNope, const void* qRope, const voi
                                  const int32_t* contextLens, const int32_t* qSeqLen, int32_t headNum,
                                  float qkScale, int32_t kvHeadNum, int maskType, int calcType,
                                  int cacheMode, int32_t batch, int32_t numBlocks, int32_t blockSize,
-                                 int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
-                                 uint64_t* workspaceSize, mpaOperation** op) {
+                                 int32_t maxBlockNum, int dtype, int64_t nTokens, void* attenOut,
+                                 float* lse, uint64_t* workspaceSize, mpaOperation** op) {
   g_last_error.clear();
   if (op) *op = nullptr;
   return make_mla_op(qNope, qRope, ctKV, kRope, blockTables, contextLens, qSeqLen, headNum, qkScale,
                      kvHeadNum, maskType, calcType, cacheMode, batch, numBlocks, blockSize, maxBlockNum,
-                     dtype, attenOut, lse, workspaceSize, op, false, nullptr, nullptr);
+                     dtype, nTokens, attenOut, lse, workspaceSize, op, false, nullptr, nullptr);
 }
 
 mpaStatus mpaMLAInt8GetWorkspaceSize(const void* qNope, const void* qRope, const void* ctKV,
@@ -491,25 +526,28 @@ mpaStatus mpaMLAInt8GetWorkspaceSize(const void* qNope, const void* qRope, const
                                      const float* qkDescale, const float* pvDescale, int32_t headNum,
                                      float qkScale, int32_t kvHeadNum, int maskType, int calcType,
                                      int32_t batch, int32_t numBlocks, int32_t blockSize,
-                                     int32_t maxBlockNum, int dtype, void* attenOut, float* lse,
-                                     uint64_t* workspaceSize, mpaOperation** op) {
+                                     int32_t maxBlockNum, int dtype, int64_t nTokens, void* attenOut,
+                                     float* lse, uint64_t* workspaceSize, mpaOperation** op) {
   g_last_error.clear();
   if (op) *op = nullptr;
   if (!kRope) return fail(MPA_ERROR_INVALID_ARG, "the int8 cache keeps the rope part in kRope: it is required");
   return make_mla_op(qNope, qRope, ctKV, kRope, blockTables, contextLens, qSeqLen, headNum, qkScale,
                      kvHeadNum, maskType, calcType, MPA_MLA_CACHE_KROPE_CTKV, batch, numBlocks, blockSize,
-                     maxBlockNum, dtype, attenOut, lse, workspaceSize, op, true, qkDescale, pvDescale);
+                     maxBlockNum, dtype, nTokens, attenOut, lse, workspaceSize, op, true, qkDescale,
+                     pvDescale);
 }
 
 mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void* stream) {
   g_last_error.clear();
   if (!op || op->kind != mpaOperation::kMla) return fail(MPA_ERROR_INVALID_ARG, "op is not an MLA operation");
-  if (workspaceSize < op->ws_bytes)
-    return fail(MPA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes, %llu needed",
-                (unsigned long long)workspaceSize, (unsigned long long)op->ws_bytes);
-  if (op->ws_bytes && !workspace) return fail(MPA_ERROR_INVALID_ARG, "workspace is NULL");
-  if (((uintptr_t)workspace) & 255) return fail(MPA_ERROR_INVALID_ARG, "workspace must be 256-byte aligned");
+  mpaStatus st = bind_workspace(op, workspace, workspaceSize, (hipStream_t)stream);
+  if (st != MPA_OK) return st;
   mpa::MlaParams p = op->mp;
+  char* ws = (char*)workspace;
+  p.segs = (const int4*)(ws + op->plan_offs[0]);
+  p.piece_seg = (const int32_t*)(ws + op->plan_offs[1]);
+  p.seqs = (const int4*)(ws + op->plan_offs[2]);
+  p.seqs2 = (const int4*)(ws + op->plan_offs[3]);
   p.part_o = (char*)workspace + op->part_o_off;
   p.part_lse = (float*)((char*)workspace + op->part_lse_off);
   hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream, op->events);
@@ -548,7 +586,7 @@ mpaStatus mpaPrefixEncoderPlanInspect(const int32_t* seqLen, const int32_t* kvSe
                                       int maskType, int32_t headNum, int32_t kvHeadNum,
                                       int32_t headSize, int32_t* items, int64_t capacity,
                                       int64_t* nItems, int32_t* rowsPerItem, int32_t* keysPerTile,
-                                      int32_t* headsPerItem) {
+                                      int32_t* headsPerItem, uint64_t* workspaceSize) {
   g_last_error.clear();
   (void)headSize;
   if (!seqLen || !kvSeqLen || batch < 1 || headNum <= 0 || kvHeadNum <= 0 || headNum % kvHeadNum)
@@ -559,6 +597,7 @@ mpaStatus mpaPrefixEncoderPlanInspect(const int32_t* seqLen, const int32_t* kvSe
   if (rowsPerItem) *rowsPerItem = plan.rows_per_item;
   if (keysPerTile) *keysPerTile = mpa::kKeysPerTile;
   if (headsPerItem) *headsPerItem = plan.heads_per_item;
+  if (workspaceSize) *workspaceSize = prefill_plan_bytes(plan.items.size(), batch);
   if (!items || capacity < (int64_t)plan.items.size())
     return fail(MPA_ERROR_INVALID_ARG, "capacity %lld < %zu items", (long long)capacity, plan.items.size());
   std::memcpy(items, plan.items.data(), plan.items.size() * sizeof(mpa::PrefillItem));

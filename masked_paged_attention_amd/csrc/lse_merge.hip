@@ -3,8 +3,9 @@
 // calcType requires; the same merge as the split-KV combine).  For row r and
 // parts s = 0 .. S-1:
 //   LSE_r = ln sum_s exp(lse[s][r]),  out[r] = sum_s exp(lse[s][r] - LSE_r) * o[s][r].
-// A part with lse = -inf (no key in its range) weighs nothing; a row whose parts
-// are all -inf gets out = 0 and LSE = -inf.
+// A part with lse = -inf (no key in its range) weighs nothing and its values are
+// not read into the sum (they may be undefined); a row whose parts are all -inf
+// gets out = 0 and LSE = -inf.
 //
 // Streaming, HBM-bound: one thread per 16-byte chunk (8 elements) of one row;
 // the threads of a row read the same LSE values (cached) and accumulate their
@@ -56,7 +57,10 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(LseMergeParams p) {
     for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
-      const float w = __builtin_amdgcn_exp2f((lk[k] - gm) * kLog2e);  // 0 for -inf parts
+      // a part with LSE = -inf is left out entirely: its values may be anything
+      // (NaN included) and must not reach the sum
+      if (lk[k] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((lk[k] - gm) * kLog2e);
       tot += w;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, (float)v[k][e], acc[e]);

@@ -707,6 +707,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
     for (int e = 0; e < 8; ++e) acc[e] *= sc;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
+      if (wgt[u] == -INFINITY) continue;  // an empty part: its values stay out of the sum
       const float wu = fast_exp2(wgt[u] - gm);
       tot += wu;
 #pragma unroll

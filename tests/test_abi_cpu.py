@@ -132,16 +132,19 @@ def test_prefill_valid_args_reach_hip_or_succeed(lib):
 def _mla(lib, **kw):
     args = dict(qn=FAKE, qr=FAKE, ckv=FAKE, kr=FAKE, bt=FAKE, ctx=[100, 300], ql=None, H=16,
                 scale=0.07, KVH=1, mask=0, calc=0, cache=1, batch=2, nb=8, bs=64, maxb=5, dtype=1,
-                out=FAKE, lse=None)
+                ntok=None, out=FAKE, lse=None)
     args.update(kw)
     ctx, pc = _i32(args["ctx"]) if args["ctx"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
     ql, pq = _i32(args["ql"]) if args["ql"] is not None else (None, ctypes.POINTER(ctypes.c_int32)())
+    ntok = args["ntok"]
+    if ntok is None:  # the token count the other arguments imply
+        ntok = int(np.sum(args["ql"])) if args["ql"] is not None and args["calc"] in (1, 3) else args["batch"]
     ws = ctypes.c_uint64(0)
     op = ctypes.c_void_p(0)
     st = lib.mpaMLAGetWorkspaceSize(args["qn"], args["qr"], args["ckv"], args["kr"], args["bt"], pc, pq,
                                     args["H"], args["scale"], args["KVH"], args["mask"], args["calc"],
                                     args["cache"], args["batch"], args["nb"], args["bs"], args["maxb"],
-                                    args["dtype"], args["out"], args["lse"], ctypes.byref(ws),
+                                    args["dtype"], ntok, args["out"], args["lse"], ctypes.byref(ws),
                                     ctypes.byref(op))
     return st, op
 
@@ -167,6 +170,8 @@ def _mla(lib, **kw):
     (dict(ctx=[100, 400]), 1),           # 7 blocks > maxBlockNum 5
     (dict(H=0), 1),
     (dict(dtype=5), 1),
+    (dict(ntok=3), 1),                   # decode: one token per sequence
+    (dict(calc=1, ql=[2, 3], ntok=4), 1),  # SPEC: sum of qSeqLen
 ])
 def test_mla_validation(lib, kw, status):
     st, op = _mla(lib, **kw)
@@ -174,9 +179,32 @@ def test_mla_validation(lib, kw, status):
     assert op.value is None or op.value == 0
 
 
+def test_mla_valid_args_reach_hip_or_succeed(lib):
+    for kw in (dict(), dict(calc=1, ql=[2, 3], mask=1), dict(calc=3, ql=[100, 7], mask=1)):
+        st, op = _mla(lib, **kw)
+        assert st in (0, 4), lib.mpaGetLastErrorMessage()
+        if st == 0:
+            assert lib.mpaDestroyOperation(op) == 0
+
+
 def test_mla_execute_rejects_small_workspace_and_wrong_op(lib):
     assert lib.mpaMLA(None, 0, None, None) == 1
     assert lib.mpaSelfAttentionPrefixEncoder(None, 0, None, None) == 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_workspace_covers_plan(seed):
+    """The workspace phase 1 asks for holds the launch plan the kernels read from
+    it: 16 bytes per workgroup item and 16 per sequence, each part 256-aligned."""
+    import masked_paged_attention_amd as mpa
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 9))
+    L = rng.integers(0, 3000, size=B)
+    P = rng.integers(0, 3000, size=B)
+    H, KVH = [(32, 8), (40, 40), (8, 1), (4, 4)][seed]
+    items, _, _, _, ws = mpa.plan_prefill(L, L + P, 9, H, KVH, with_workspace=True)
+    need = -(-16 * len(items) // 256) * 256 + -(-16 * B // 256) * 256
+    assert ws == need and ws >= 16 * (len(items) + B) and ws % 256 == 0
 
 
 def test_launch_events_need_an_operation(lib):
@@ -334,13 +362,13 @@ def test_compressed_mask_valid_args_reach_hip_or_succeed(lib):
             assert lib.mpaDestroyOperation(op) == 0
 
 
-def _mla8(lib, qkd=FAKE, pvd=FAKE, kr=FAKE, KVH=1, calc=0, ql=None, dtype=1):
+def _mla8(lib, qkd=FAKE, pvd=FAKE, kr=FAKE, KVH=1, calc=0, ql=None, dtype=1, ntok=2):
     ctx, pc = _i32([100, 300])
     pq = _i32(ql)[1] if ql is not None else ctypes.POINTER(ctypes.c_int32)()
     ws = ctypes.c_uint64(0)
     op = ctypes.c_void_p(0xdead)
     st = lib.mpaMLAInt8GetWorkspaceSize(FAKE, FAKE, FAKE, kr, FAKE, pc, pq, qkd, pvd, 16, 0.07, KVH,
-                                        0, calc, 2, 8, 64, 5, dtype, FAKE, None,
+                                        0, calc, 2, 8, 64, 5, dtype, ntok, FAKE, None,
                                         ctypes.byref(ws), ctypes.byref(op))
     return st, op
 
@@ -349,6 +377,7 @@ def _mla8(lib, qkd=FAKE, pvd=FAKE, kr=FAKE, KVH=1, calc=0, ql=None, dtype=1):
     (dict(qkd=None), 1), (dict(pvd=None), 1), (dict(kr=None), 1), (dict(KVH=2), 2),
     (dict(calc=1), 1),                   # SPEC without qSeqLen
     (dict(dtype=2), 1),
+    (dict(ntok=1), 1),                   # one token per sequence
 ])
 def test_mla_int8_validation(lib, kw, status):
     st, op = _mla8(lib, **kw)

@@ -1,19 +1,21 @@
 """Benchmark of the masked paged-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-  * prefill: the prefix-encoder causal GQA workload (batch 8, seqLen ~ U[128,1024],
-    cached prefix ~ U[0,2048], 32 query / 8 KV heads, headSize 128, blockSize 128,
-    bf16), one PrefixEncoder launch;
+  * prefill: one 16384-token sequence (no prefix), 40 query / 40 KV heads,
+    headSize 128, blockSize 128, bf16, ALiBi slopes 2^(-8(h+1)/40): one
+    PrefixEncoder launch with the sqrt ALiBi mask and one with the left-aligned
+    ALiBi mask, over the same inputs;
   * decode: MLA on the latent paged cache (batch 64, 128 heads, q_len 1, 576/512,
     blockSize 128, contextLens ~ U[1024,8192], bf16), split + combine, reading one
     of two rotated KV caches (2 x 340 MB > the 256 MB Infinity Cache) so the cache
     is cold.
-value = valid prefill FLOPs (4 * headSize per visible (query, key) pair) / prefill
-kernel time; the decode rate (algorithmic bytes / MLA call time) is reported
-beside it.  Kernel times come from HIP events that each call records on its own
-kernels' dispatch packets (start of its first kernel, end of its last) inside the
-timed region, so no event command sits between the kernels on the stream; the
-step time comes from two stream events around the whole timed region.
+value = valid prefill FLOPs of the two launches (4 * headSize per visible
+(query, key) pair) / their kernel time; the decode rate (algorithmic bytes / MLA
+call time) is reported beside it.  Kernel times come from HIP events that each
+call records on its own kernels' dispatch packets (start of its first kernel,
+end of its last) inside the timed region, so no event command sits between the
+calls on the stream; the step time comes from two stream events around the whole
+timed region (it includes each call's copy of its launch plan into its workspace).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
 """
@@ -120,7 +122,7 @@ KERNEL_FILES = ("masked_paged_attention_amd/csrc/prefill_fwd.hip",
                 "masked_paged_attention_amd/csrc/kernels.h",
                 "masked_paged_attention_amd/csrc/planner.cpp",
                 "masked_paged_attention_amd/csrc/api.cpp")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_alibi16384_mla_decode.txt")
 KERNEL_KEYS = ("prefill_dma_kernel", "prefill_fwd_kernel", "mla_split_kernel", "mla_combine_kernel")
 
 
@@ -306,45 +308,70 @@ def time_ops(torch, ops, iters, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def cpu_baseline(budget_s=12.0):
-    """The fp64 oracle, as it is, on a bounded sample of the prefill workload: whole
-    (sequence, head) pairs in a seeded order, passing over the workload again when
-    it is done, until the time budget is spent."""
+_CPU_CASE = None  # oracle arguments of the workload the CPU baseline samples (set before forking)
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    global _CPU_LIMIT
+    _CPU_LIMIT = threadpool_limits(1)  # one BLAS thread per worker process
+
+
+def _cpu_pair(bh):
+    """Oracle output of every row of one (sequence, head) pair; returns the pair's
+    valid FLOPs."""
     import oracle
-    import workloads as W
+    b, h = bh
+    args = _CPU_CASE
+    L = int(args["seq_len"][b])
+    oracle.prefix_encoder_rows(rows=[(b, i, h) for i in range(L)], **args)
+    return prefill_valid_flops([L], [int(args["kv_seq_len"][b])], True, 1, args["query"].shape[-1])
+
+
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    c = W.make_prefill_config("prefix_gqa_causal")
-    args = c.oracle_args()
-    rng = np.random.default_rng(0)
-    pairs = [(b, h) for b in range(c.batch) for h in range(c.head_num)]
-    order = rng.permutation(len(pairs))
-    done_flops = 0
-    done = 0
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, name, max_workers=16, max_pairs=40):
+    """The fp64 oracle, as it is, on a bounded sample of the workload: up to
+    max_pairs whole (sequence, head) pairs (every row of the pair; for the
+    16384-token workload that is all 40 heads), spread over worker processes
+    with one BLAS thread each, as many workers as the host allows (at most
+    max_workers), timed by the wall clock."""
+    import multiprocessing as mp
+    global _CPU_CASE
+    _CPU_CASE = case.oracle_args()
+    n_cpu = os.cpu_count() or 1
+    workers = max(1, min(max_workers, n_cpu))
+    pairs = [(b, h) for b in range(case.batch) for h in range(case.head_num)]
+    order = np.random.default_rng(0).permutation(len(pairs))[:max_pairs]
+    todo = [pairs[k] for k in order]
+    ctx = mp.get_context("fork")
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 <= budget_s:
-        for k in order:
-            b, h = pairs[k]
-            L = int(c.seq_len[b])
-            rows = [(b, i, h) for i in range(L)]
-            oracle.prefix_encoder_rows(rows=rows, **args)
-            done_flops += prefill_valid_flops([L], [c.kv_seq_len[b]], True, 1, c.head_size)
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        flops = sum(pool.map(_cpu_pair, todo, chunksize=1))
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} (sequence, head) pairs of the prefix-encoder GQA workload "
-                      f"({len(pairs)} per pass, {done / len(pairs):.1f} passes), all rows each, "
-                      f"fp64 numpy, {dt:.1f} s"}
+    _CPU_CASE = None
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(todo)} whole (sequence, head) pairs of the {name} workload, all rows each "
+                      f"({len(todo)} of {len(pairs)} pairs; fp64 numpy), {workers} worker processes "
+                      f"x 1 BLAS thread, {dt:.1f} s wall",
+            "cpu_model": _cpu_model(), "os_cpu_count": n_cpu, "threads_per_worker": 1,
+            "seconds": round(dt, 2), "valid_flops": int(flops)}
 
 
 def _sum_or_none(*xs):
     return None if any(x is None for x in xs) else int(sum(xs))
+
+
+# The step's prefill workload (the sqrt call; the left-aligned call reads the same inputs).
+HEADLINE = "alibi_sqrt_16384"
 
 
 def main():
@@ -379,12 +406,23 @@ def main():
         sys.exit(2)
 
     import torch
-    import masked_paged_attention_amd as mpa
     import workloads as W
 
+    # Inputs of the headline prefill workload, generated on the host; the CPU
+    # baseline runs the oracle on them before anything touches the GPU (its
+    # worker processes are forked from this one).
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    hc = W.make_prefill_config(HEADLINE)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(hc, "1 x 16384-token sqrt ALiBi (40 heads, headSize 128, bf16)")
+        print(f"bench: cpu baseline {cpu['value']:.3e} TFLOP/s on {cpu['cores']} processes "
+              f"({cpu['seconds']} s)", file=sys.stderr, flush=True)
+
+    import masked_paged_attention_amd as mpa
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print("bench: generating inputs", file=sys.stderr, flush=True)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -393,13 +431,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # --- prefill workload ---
-    pc = W.make_prefill_config("prefix_gqa_causal", device=dev)
+    # --- prefill: the 16384-token sequence, sqrt and left-aligned ALiBi (same inputs) ---
+    pc = hc.to(dev)
+    del hc
     p_out = torch.empty_like(pc.query)
     p_lse = torch.empty((pc.n_tokens, pc.head_num), dtype=torch.float32, device=dev)
-    p_op = mpa.PrefixEncoder(pc.query, pc.key, pc.value, pc.block_tables, pc.seq_len, pc.kv_seq_len,
-                             mask_type=pc.mask_type, qk_scale=pc.qk_scale, out=p_out, lse=p_lse)
-    p_flops = prefill_valid_flops(pc.seq_len, pc.kv_seq_len, True, pc.head_num, pc.head_size)
+    p_slopes = torch.as_tensor(pc.slopes, device=dev)
+    p_ops = [mpa.PrefixEncoder(pc.query, pc.key, pc.value, pc.block_tables, pc.seq_len, pc.kv_seq_len,
+                               mask_type=mt, qk_scale=pc.qk_scale, slopes=p_slopes, out=p_out, lse=p_lse)
+             for mt in (mpa.MASK_ALIBI_SQRT, mpa.MASK_ALIBI_LEFT)]
+    p_flops = prefill_valid_flops(pc.seq_len, pc.kv_seq_len, True, pc.head_num, pc.head_size)  # per call
 
     # --- decode workload: two independent caches, rotated per step ---
     mcs = [W.make_mla_config("mla_decode_q1", device=dev)]
@@ -423,19 +464,21 @@ def main():
 
     # Per-call times come from events recorded on the calls' own kernels (start of
     # the first, end of the last: mpaOperationSetLaunchEvents), so nothing but the
-    # kernels sits on the stream inside the timed region.
+    # calls' own commands sits on the stream inside the timed region.
     def step(i, ev=None):
         if ev is not None:
-            p_op.set_launch_events(*ev[0])
-            m_ops[i % 2].set_launch_events(*ev[1])
-        p_op.run()
+            for op, e in zip(p_ops, ev[:2]):
+                op.set_launch_events(*e)
+            m_ops[i % 2].set_launch_events(*ev[2])
+        for op in p_ops:
+            op.run()
         m_ops[i % 2].run()
 
     print("bench: warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [launch_events(torch, 2) for _ in range(args.steps)]
+    evs = [launch_events(torch, 3) for _ in range(args.steps)]
     t_start, t_end = _events(torch)
     torch.cuda.synchronize()
     t_start.record()
@@ -444,66 +487,75 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    p_ms = float(np.mean([p[0].elapsed_time(p[1]) for p, _ in evs]))
-    m_ms = float(np.mean([m[0].elapsed_time(m[1]) for _, m in evs]))
-    p_op.set_launch_events(None, None)
-    for op in m_ops:
+    sq_ms = float(np.mean([e[0][0].elapsed_time(e[0][1]) for e in evs]))
+    lf_ms = float(np.mean([e[1][0].elapsed_time(e[1][1]) for e in evs]))
+    m_ms = float(np.mean([e[2][0].elapsed_time(e[2][1]) for e in evs]))
+    for op in p_ops + m_ops:
         op.set_launch_events(None, None)
-    p_tflops = p_flops / (p_ms * 1e-3) / 1e12
+    p_tflops = 2 * p_flops / ((sq_ms + lf_ms) * 1e-3) / 1e12
+    sq_tf = p_flops / (sq_ms * 1e-3) / 1e12
+    lf_tf = p_flops / (lf_ms * 1e-3) / 1e12
     m_gbs = m_bytes / (m_ms * 1e-3) / 1e9
-    print(f"bench: prefill {p_ms:.4f} ms {p_tflops:.1f} TFLOP/s; decode {m_ms:.4f} ms {m_gbs:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    print(f"bench: prefill sqrt {sq_ms:.4f} ms {sq_tf:.1f} TFLOP/s, left {lf_ms:.4f} ms {lf_tf:.1f} TFLOP/s; "
+          f"decode {m_ms:.4f} ms {m_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    # the dominant kernel of the step: the slower of the two prefill launches
+    dom_name, dom_ms, dom_tf = max([("prefill_dma_kernel<bf16,4>", sq_ms, sq_tf),
+                                    ("prefill_dma_kernel<bf16,5>", lf_ms, lf_tf)], key=lambda x: x[1])
+    del pc, p_out, p_lse, p_ops
+    torch.cuda.empty_cache()
 
     extra = {}
     if not args.no_extra:
-        for name in ["alibi_right_4x4096", "alibi_sqrt_16384", "alibi_left_16384",
-                     "alibi_sqrt_varlen16", "alibi_sqrt_padded16"]:
-            print(f"bench: extra {name}", file=sys.stderr, flush=True)
-            c = W.make_prefill_config(name, device=dev)
+        def prefill_extra(name, c, tile=None, fl=None):
             sl = torch.as_tensor(c.slopes, device=dev) if c.slopes is not None else None
             op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
                                    mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
-                                   q_start_loc=c.q_start_loc, return_lse=True)
+                                   q_start_loc=c.q_start_loc, return_lse=True, compressed_mask=tile,
+                                   attention_chunk=c.chunk if c.chunk else None)
             ms = time_ops(torch, [op], 10, 3)
-            fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
+            if fl is None:
+                fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
             tf = fl / (ms * 1e-3) / 1e12
             e = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_MFMA_TFLOPS, 4)}
             if c.q_start_loc is not None:
                 e["padding_positions"] = padding_positions(c.seq_len, 8192)
             extra[name] = e
             op.close()
-            del c, op
             torch.cuda.empty_cache()
-        # the same calls reading the page's compressed mask tile instead of generating
-        # the mask (one global read per 4 scores)
-        for name, cfg in [("prefix_gqa_causal_norm_tile", None), ("alibi_right_4x4096_tile", "alibi_right_4x4096")]:
+
+        # the prefix-encoder causal GQA workload, then the same call reading the
+        # page's compressed norm tile
+        print("bench: extra prefix_gqa_causal", file=sys.stderr, flush=True)
+        c = W.make_prefill_config("prefix_gqa_causal", device=dev)
+        prefill_extra("prefix_gqa_causal", c)
+        prefill_extra("prefix_gqa_causal_norm_tile", c, W.compressed_tile(c.mask_type, c.dtype).to(dev))
+        extra["prefix_gqa_causal"]["valid_flops"] = int(
+            prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size))
+        del c
+        print("bench: extra alibi_right_4x4096", file=sys.stderr, flush=True)
+        c = W.make_prefill_config("alibi_right_4x4096", device=dev)
+        prefill_extra("alibi_right_4x4096", c)
+        prefill_extra("alibi_right_4x4096_tile", c, W.compressed_tile(c.mask_type, c.dtype).to(dev))
+        del c
+        # the 16384-token calls reading the [256,256] compressed tiles
+        for name in ["alibi_sqrt_16384", "alibi_left_16384"]:
+            print(f"bench: extra {name}_tile", file=sys.stderr, flush=True)
+            c = W.make_prefill_config(name, device=dev)
+            prefill_extra(name + "_tile", c, W.compressed_tile(c.mask_type, c.dtype).to(dev))
+            del c
+        for name in ["alibi_sqrt_varlen16", "alibi_sqrt_padded16", "alibi_left_varlen16", "alibi_left_padded16"]:
             print(f"bench: extra {name}", file=sys.stderr, flush=True)
-            c = pc if cfg is None else W.make_prefill_config(cfg, device=dev)
-            tile = W.compressed_tile(c.mask_type, c.dtype).to(dev)
-            sl = torch.as_tensor(c.slopes, device=dev) if c.slopes is not None else None
-            op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
-                                   mask_type=c.mask_type, qk_scale=c.qk_scale, slopes=sl,
-                                   q_start_loc=c.q_start_loc, return_lse=True, compressed_mask=tile)
-            ms = time_ops(torch, [op], 10, 3)
-            fl = prefill_valid_flops(c.seq_len, c.kv_seq_len, True, c.head_num, c.head_size)
-            extra[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                           "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
-            op.close()
-            del c, op, tile
-            torch.cuda.empty_cache()
+            c = W.make_prefill_config(name, device=dev)
+            prefill_extra(name, c)
+            del c
         # chunked local causal mask over one 16384-token bf16 sequence, 40 heads, chunk 2048
         print("bench: extra chunked_16384_c2048", file=sys.stderr, flush=True)
         cc = W.make_prefill(87, np.array([16384]), np.array([16384]), 40, 40, 128, 128, "bf16", 9,
                             1.0 / np.sqrt(128.0), chunk=2048).to(dev)
-        op = mpa.PrefixEncoder(cc.query, cc.key, cc.value, cc.block_tables, cc.seq_len, cc.kv_seq_len,
-                               mask_type=cc.mask_type, qk_scale=cc.qk_scale, return_lse=True,
-                               attention_chunk=cc.chunk)
-        ms = time_ops(torch, [op], 10, 3)
-        fl = prefill_valid_flops_chunked(cc.seq_len, cc.kv_seq_len, cc.chunk, cc.head_num, cc.head_size)
-        extra["chunked_16384_c2048"] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                                        "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
-        op.close()
-        del cc, op
+        prefill_extra("chunked_16384_c2048", cc,
+                      fl=prefill_valid_flops_chunked(cc.seq_len, cc.kv_seq_len, cc.chunk, cc.head_num,
+                                                     cc.head_size))
+        del cc
         print("bench: extra mla_spec_q4", file=sys.stderr, flush=True)
         m4 = W.make_mla_config("mla_spec_q4", device=dev)
         op4 = mpa.MLA(m4.q_nope, m4.q_rope, m4.ct_kv, m4.k_rope, m4.block_tables, m4.context_lens,
@@ -516,6 +568,7 @@ def main():
                                 "frac_mfma": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
                                 "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
         op4.close()
+        del m4, op4
         # MLA calcType PREFILL: 4 prompts of 256 new tokens over 1-4k keys, causal.
         print("bench: extra mla_prefill", file=sys.stderr, flush=True)
         ctx_p = np.array([1024, 2048, 3072, 4096], dtype=np.int32)
@@ -553,28 +606,22 @@ def main():
         for op8 in ops8:
             op8.close()
         del m8, ops8, o8, l8
-        # LSE merge of 8 partials shaped like the prefix-encoder output (HBM-bound;
-        # 8 x 43 MB of partials exceed the 256 MB Infinity Cache).
+        # LSE merge of 8 partials shaped like the prefix-encoder workload's output
+        # (4624 tokens x 32 heads x 128; HBM-bound; 8 x 38 MB of partials)
         print("bench: extra lse_merge", file=sys.stderr, flush=True)
-        n_parts = 8
-        rows = pc.n_tokens * pc.head_num
+        n_parts, n_tok, n_h, hd = 8, 4624, 32, 128
+        rows = n_tok * n_h
         g = torch.Generator(device=dev).manual_seed(5)
-        o_parts = torch.randn((n_parts, pc.n_tokens, pc.head_num, pc.head_size), generator=g,
-                              device=dev).to(torch.bfloat16)
-        l_parts = torch.randn((n_parts, pc.n_tokens, pc.head_num), generator=g, device=dev) * 4.0
+        o_parts = torch.randn((n_parts, n_tok, n_h, hd), generator=g, device=dev).to(torch.bfloat16)
+        l_parts = torch.randn((n_parts, n_tok, n_h), generator=g, device=dev) * 4.0
         mo = torch.empty_like(o_parts[0])
         ml = torch.empty_like(l_parts[0])
         ms = time_op(torch, lambda: mpa.lse_merge(o_parts, l_parts, out=mo, lse=ml), 20, 3)
-        by = (n_parts + 1) * rows * (pc.head_size * 2 + 4)
+        by = (n_parts + 1) * rows * (hd * 2 + 4)
         extra["lse_merge"] = {"ms": round(ms, 4), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                              "parts": n_parts, "rows": rows, "head_dim": pc.head_size}
+                              "parts": n_parts, "rows": rows, "head_dim": hd}
         del o_parts, l_parts, mo, ml
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
 
     res = {
         "metric": METRIC,
@@ -590,23 +637,33 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "prefix-encoder causal GQA prefill (batch 8, seqLen~U[128,1024], prefix~U[0,2048], "
-                        "32/8 heads, headSize 128, blockSize 128, bf16) + MLA decode (batch 64, 128 heads, "
-                        "q_len 1, 576/512, blockSize 128, contextLens~U[1024,8192], bf16, cold KV)",
-            "prefill_tokens": int(pc.seq_len.sum()),
-            "prefill_valid_flops": int(p_flops),
+            "workload": "long-sequence ALiBi prefill: 1 x 16384 tokens (no prefix), 40/40 heads, headSize 128, "
+                        "blockSize 128, bf16, slopes 2^(-8(h+1)/40), one sqrt-ALiBi call and one left-aligned "
+                        "ALiBi call per step (value = valid FLOPs of both / their kernel time) + MLA decode "
+                        "(batch 64, 128 heads, q_len 1, 576/512, blockSize 128, contextLens~U[1024,8192], "
+                        "bf16, cold KV)",
+            "prefill_tokens": 16384,
+            "prefill_valid_flops_per_call": int(p_flops),
             "decode_batch": int(m0.batch),
             "decode_kv_keys": int(np.sum(m0.context_lens)),
         },
-        "roofline": {"bound": "mfma", "kernel": "prefill_dma_kernel<bf16,causal>",
-                     "achieved": round(p_tflops, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(p_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": read_traffic("prefill_dma_kernel"),
-                     "per_launch_flops": int(p_flops), "ms": round(p_ms, 5)},
+        "roofline": {"bound": "mfma", "kernel": dom_name,
+                     "achieved": round(dom_tf, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tf / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": read_traffic(dom_name),
+                     "per_launch_flops": int(p_flops), "ms": round(dom_ms, 5)},
+        "prefill": {"sqrt": {"ms": round(sq_ms, 5), "tflops": round(sq_tf, 1),
+                             "frac_mfma": round(sq_tf / PEAK_MFMA_TFLOPS, 4),
+                             "traffic": read_traffic("prefill_dma_kernel<bf16,4>")},
+                    "left": {"ms": round(lf_ms, 5), "tflops": round(lf_tf, 1),
+                             "frac_mfma": round(lf_tf / PEAK_MFMA_TFLOPS, 4),
+                             "traffic": read_traffic("prefill_dma_kernel<bf16,5>")},
+                    "target": "50% of dense bf16 MFMA peak (<= 2.2 ms per call)"},
         "decode": {"value": round(m_gbs, 1), "unit": "GB/s", "frac_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
                    "ms": round(m_ms, 5), "bytes": int(m_bytes),
                    "tflops": round(m_flops / (m_ms * 1e-3) / 1e12, 1),
                    "traffic": _sum_or_none(read_traffic("mla_split_kernel"), read_traffic("mla_combine_kernel")),
+                   "target": "70% of HBM",
                    "note": "whole MLA call (split + combine kernels)"},
         "extra": extra,
         "cpu_baseline": cpu,

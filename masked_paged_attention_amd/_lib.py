@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libmpa.so")
+# MPA_LIBRARY names another build of the same library (e.g. to compare builds);
+# by default the in-tree one.
+LIB_PATH = os.environ.get("MPA_LIBRARY") or os.path.join(_HERE, "lib", "libmpa.so")
 
 c_i32p = ctypes.POINTER(ctypes.c_int32)
 c_i64p = ctypes.POINTER(ctypes.c_int64)

@@ -16,6 +16,8 @@ call records on its own kernels' dispatch packets (start of its first kernel,
 end of its last) inside the timed region, so no event command sits between the
 calls on the stream; the step time comes from two stream events around the whole
 timed region (it includes each call's copy of its launch plan into its workspace).
+Before the W warm-up steps the step runs untimed for half a second, so that the
+timed steps see the GPU's working clocks rather than its ramp from idle.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
 """
@@ -372,6 +374,7 @@ def _sum_or_none(*xs):
 
 # The step's prefill workload (the sqrt call; the left-aligned call reads the same inputs).
 HEADLINE = "alibi_sqrt_16384"
+PREWARM_S = 0.5  # untimed steps before the warm-up steps (clock ramp)
 
 
 def main():
@@ -474,7 +477,14 @@ def main():
             op.run()
         m_ops[i % 2].run()
 
-    print("bench: warmup", file=sys.stderr, flush=True)
+    # The GPU leaves its idle clocks over the first few tens of milliseconds of
+    # work (the first calls of a fresh process run up to 3x slower): the step runs
+    # untimed for PREWARM_S seconds before the W warm-up steps.
+    print("bench: clock pre-warm + warmup", file=sys.stderr, flush=True)
+    t_pw = time.perf_counter()
+    while time.perf_counter() - t_pw < PREWARM_S:
+        step(0)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

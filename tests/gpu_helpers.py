@@ -94,6 +94,19 @@ def check_prefill_sampled(case, out, lse, n=192, seed=0):
     compare_rows(case.name + " (sampled)", case.dtype, o, l, ro, rl)
 
 
+def check_prefill_heads(case, out, lse, heads):
+    """Element-wise parity on every row of the given heads, all sequences."""
+    args = case.oracle_args()
+    rows = [(b, i, h) for h in heads for b in range(case.batch) for i in range(int(case.seq_len[b]))]
+    ro, rl = oracle.prefix_encoder_rows(rows=rows, **args)
+    starts = case.row_starts()
+    toks = torch.as_tensor([starts[b] + i for b, i, _ in rows], device=out.device)
+    hs = torch.as_tensor([h for _, _, h in rows], device=out.device)
+    o = out[toks, hs].float().cpu().numpy()
+    l = lse[toks, hs].cpu().numpy() if lse is not None else None
+    compare_rows(f"{case.name} (heads {list(heads)}, every row)", case.dtype, o, l, ro, rl)
+
+
 def gpu_mla(case, return_lse=True):
     import masked_paged_attention_amd as mpa
     lse = None

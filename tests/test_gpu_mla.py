@@ -58,6 +58,12 @@ def test_full_size_sampled(name):
                   {(0, 0), (T - 1, H - 1)})
     check_mla(c, out, lse, rows=rows)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    # every head of every token of two whole sequences: the shortest and the longest
+    qlens = [1] * c.batch if c.q_seq_len is None else [int(x) for x in c.q_seq_len]
+    tok0 = np.concatenate([[0], np.cumsum(qlens)[:-1]])
+    for b in (int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))):
+        rows = [(int(tok0[b]) + t, h) for t in range(qlens[b]) for h in range(H)]
+        check_mla(c, out, lse, rows=rows)
 
 
 def test_many_short_sequences():
@@ -160,6 +166,12 @@ def test_int8_full_size_sampled():
                   {(0, 0), (T - 1, H - 1)})
     check_mla(c, out, lse, rows=rows)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    # every head of every token of two whole sequences: the shortest and the longest
+    qlens = [1] * c.batch if c.q_seq_len is None else [int(x) for x in c.q_seq_len]
+    tok0 = np.concatenate([[0], np.cumsum(qlens)[:-1]])
+    for b in (int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens))):
+        rows = [(int(tok0[b]) + t, h) for t in range(qlens[b]) for h in range(H)]
+        check_mla(c, out, lse, rows=rows)
 
 
 def test_int8_prefill_and_determinism():

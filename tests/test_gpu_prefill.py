@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import (check_prefill_full, check_prefill_sampled, gpu_prefill, log)
+from gpu_helpers import (check_prefill_full, check_prefill_heads, check_prefill_sampled, gpu_prefill, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,28 @@ def test_small_all_masks(dtype, D, mask):
     bs = {64: 16, 128: 24}[D]
     log(f"case small dtype={dtype} D={D} mask={mask} bs={bs}")
     c = _case(10 + mask + D, [150, 67, 1], [0, 90, 200], 4, 2, D, bs, dtype, mask)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("bs", [64, 128, 256])
+@pytest.mark.parametrize("mask", [0, 3, 4, 5, 9])
+def test_head_size_64_whole_tile_blocks(dtype, bs, mask):
+    # headSize 64 with a power-of-two blockSize >= 64: every 64-key tile inside one
+    # cache block (one block id per tile, fetched ahead) -- random block
+    # permutation, NaN in every slot that must not be read
+    log(f"case D=64 bs={bs} dtype={dtype} mask={mask}")
+    c = _case(300 + bs + mask, [333, 70, 1], [90, 400, 250], 4, 2, 64, bs, dtype, mask)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("bs", [64, 256])
+def test_head_size_64_whole_tile_blocks_chunked(bs):
+    log(f"case D=64 bs={bs} chunked")
+    c = W.make_prefill(310 + bs, np.array([300, 200]), np.array([800, 200]), 8, 2, 64, bs, "bf16", 9,
+                       0.125, poison=True, chunk=96, name=f"chunk96-D64-bs{bs}").to(DEV)
     out, lse = gpu_prefill(c)
     check_prefill_full(c, out, lse)
 
@@ -126,10 +148,13 @@ def test_gqa_equals_mha_with_repeated_kv():
 @pytest.mark.parametrize("name", ["prefix_gqa_causal", "alibi_right_4x4096", "alibi_sqrt_16384",
                                   "alibi_left_16384", "alibi_sqrt_varlen16", "alibi_left_padded16"])
 def test_full_size_configs_sampled(name):
+    # sampled rows of every head, then every row of the first and the last head
+    # (the launch configuration the benchmark times)
     log(f"case full-size {name}")
     c = W.make_prefill_config(name, poison=True, device=DEV)
     out, lse = gpu_prefill(c)
     check_prefill_sampled(c, out, lse, n=160, seed=1)
+    check_prefill_heads(c, out, lse, [0, c.head_num - 1])
 
 
 def test_packed_equals_padded_full_size():

@@ -660,3 +660,110 @@ def test_mla_int8_descale_invariants():
     o4, l4 = oracle.mla(**a4)
     np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(l3, l4, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Attention read through an explicit compressed tile (the mask_tile branch of
+# oracle.prefix_encoder / prefix_encoder_rows).
+# ---------------------------------------------------------------------------
+
+_PAGE_TILES = {M.MASK_CAUSAL: M.compressed_norm, M.MASK_ALIBI: M.compressed_alibi,
+               M.MASK_ALIBI_SQRT: M.compressed_alibi, M.MASK_ALIBI_LEFT: M.compressed_alibi_left}
+
+
+@pytest.mark.parametrize("mt", [M.MASK_CAUSAL, M.MASK_ALIBI, M.MASK_ALIBI_SQRT, M.MASK_ALIBI_LEFT])
+def test_prefix_encoder_with_page_tile_equals_generated_rule(mt):
+    """The tiles as the compressed-mask page describes them, read through the
+    tile branch, give the attention of the generated rule of the same type --
+    with cached prefixes, so rows and keys span several 128-position blocks."""
+    rng = np.random.default_rng(600 + mt)
+    L, P = np.array([150, 70]), np.array([140, 300])
+    kv = L + P
+    H, KVH, D = 4, 2, 8
+    q, k, v, bt, _ = _case(rng, 2, L, kv, H, KVH, D, 32)
+    slopes = (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32) if mt != M.MASK_CAUSAL else None
+    args = dict(query=q, key=k, value=v, block_tables=bt, seq_len=L, kv_seq_len=kv, slopes=slopes,
+                mask_type=mt, head_num=H, kv_head_num=KVH, qk_scale=0.3)
+    o_gen, l_gen = oracle.prefix_encoder(**args)
+    o_tile, l_tile = oracle.prefix_encoder(mask_tile=_PAGE_TILES[mt](), **args)
+    np.testing.assert_allclose(o_tile, o_gen, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_tile, l_gen, rtol=0, atol=1e-12)
+
+
+def _tile_pair(mt, tile, slope, a, j, kv):
+    """The expansion of a compressed tile for one (query position a, key j), as
+    the operation's contract states it: (visible, bias)."""
+    T = 128
+    if j >= kv:
+        return False, 0.0
+    bq, r, bk, c = a // T, a % T, j // T, j % T
+    dk = bq - bk
+    if dk < 0:
+        return False, 0.0
+    if mt == M.MASK_CAUSAL:
+        if dk > 0:
+            return True, 0.0
+        y = float(tile[r][c])
+        return (y != -math.inf), y
+    y = float(tile[r][c] if dk == 0 else tile[T + r][c])
+    if y == -math.inf:
+        return False, 0.0
+    if mt == M.MASK_ALIBI_LEFT:
+        return True, slope * (y + T * bk)
+    if dk >= 1:
+        y -= T * (dk - 1)
+    if mt == M.MASK_ALIBI:
+        return True, slope * y
+    return True, -slope * math.sqrt(-y)
+
+
+@pytest.mark.parametrize("mt", [M.MASK_CAUSAL, M.MASK_ALIBI, M.MASK_ALIBI_SQRT, M.MASK_ALIBI_LEFT])
+def test_prefix_encoder_with_perturbed_tile_brute_force(mt):
+    """Arbitrary tile contents (extra bias, -inf holes that hide keys): the tile
+    branch against a pure-Python pass, one (row, key) pair at a time."""
+    rng = np.random.default_rng(700 + mt)
+    T = 128
+    n = T if mt == M.MASK_CAUSAL else 2 * T
+    x = np.arange(n)[:, None]
+    y = np.arange(n)[None, :]
+    base = {M.MASK_CAUSAL: np.zeros((n, n)), M.MASK_ALIBI: (y - x).astype(float),
+            M.MASK_ALIBI_SQRT: (y - x).astype(float), M.MASK_ALIBI_LEFT: np.broadcast_to(y, (n, n)).astype(float)}[mt]
+    extra = rng.integers(-12, 1, size=(n, n)) / 4.0  # keeps the distance form <= 0
+    tile = np.where(y <= x, base + extra, -np.inf)
+    tile[(rng.random((n, n)) < 0.05) & (y < x)] = -np.inf
+    L, P = np.array([40, 9]), np.array([230, 120])
+    kv = L + P
+    H, KVH, D = 2, 1, 4
+    q, k, v, bt, _ = _case(rng, 2, L, kv, H, KVH, D, 16)
+    slopes = np.array([0.75, 0.1], dtype=np.float32)
+    scale = 0.4
+    o, lse = oracle.prefix_encoder(q, k, v, bt, L, kv, slopes if mt != M.MASK_CAUSAL else None, mt, H, KVH,
+                                   scale, mask_tile=tile)
+    bs = k.shape[1]
+    sc = float(np.float32(scale))
+    starts = [0, int(L[0])]
+    for b in range(2):
+        for h in range(H):
+            sl = float(np.float32(slopes[h])) if mt != M.MASK_CAUSAL else 0.0
+            for i in range(int(L[b])):
+                a = int(kv[b] - L[b]) + i
+                qq = q[starts[b] + i][h]
+                ss, vv = [], []
+                for j in range(int(kv[b])):
+                    vis, bias = _tile_pair(mt, tile, sl, a, j, int(kv[b]))
+                    if not vis:
+                        continue
+                    blk = int(bt[b][j // bs])
+                    dot = math.fsum(float(qq[d]) * float(k[blk][j % bs][0][d]) for d in range(D))
+                    ss.append(sc * dot + bias)
+                    vv.append(v[blk][j % bs][0])
+                got_o, got_l = o[starts[b] + i][h], lse[starts[b] + i][h]
+                if not ss:
+                    assert got_l == -math.inf and np.all(got_o == 0.0)
+                    continue
+                m = max(ss)
+                w = [math.exp(s - m) for s in ss]
+                tot = math.fsum(w)
+                want = [math.fsum(w[t] * float(vv[t][d]) for t in range(len(w))) / tot for d in range(D)]
+                np.testing.assert_allclose(got_o, want, rtol=0, atol=1e-12)
+                assert abs(got_l - (m + math.log(tot))) <= 1e-12 * max(1.0, abs(got_l))

@@ -270,6 +270,26 @@ mpaStatus mpaMLAInt8GetWorkspaceSize(
 mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void *stream);
 
 /*
+ * MLA, phase 2, without any allocation: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it).  The same launches as mpaMLA, with the plan and the split-KV
+ * partials in a buffer the library owns: a static device array of
+ * MPA_MLA_STATIC_SCRATCH_BYTES bytes (64 MiB), one per GPU, held until the
+ * process ends.  Nothing is allocated and nothing must be zeroed: every
+ * execution first copies its plan into the buffer and writes every partial it
+ * reads.  All executions on one GPU share that GPU's buffer: executions that
+ * may overlap on one GPU (different streams, or streams of different threads)
+ * race and must be serialised by the caller.
+ *   op      an operation from mpaMLAGetWorkspaceSize / mpaMLAInt8GetWorkspaceSize
+ *           whose workspace size is at most MPA_MLA_STATIC_SCRATCH_BYTES
+ *   stream  hipStream_t of the launches
+ * Errors: MPA_ERROR_INVALID_ARG (op NULL or not MLA), MPA_ERROR_WORKSPACE_TOO_SMALL
+ * (the operation needs more than the static buffer: use mpaMLA), MPA_ERROR_HIP.
+ */
+#define MPA_MLA_STATIC_SCRATCH_BYTES (64ull << 20)
+mpaStatus mpaMLAStaticScratch(mpaOperation *op, void *stream);
+
+/*
  * Merge of attention partials over disjoint key ranges by their log-sum-exp
  * (page "MLA", parameter table: the lse output, which the RING calcType requires;
  * the same merge the MLA call applies to its split-KV partials).  Each part is

@@ -309,6 +309,14 @@ class MLA:
         _check(st, "mpaMLA")
         return (self.out, self.lse) if self.lse is not None else self.out
 
+    def run_static_scratch(self, stream=None):
+        """The same launches with the plan and partials in the library's static
+        device buffer instead of the workspace (mpaMLAStaticScratch: nothing is
+        allocated; executions that overlap on one GPU race)."""
+        st = LIB.mpaMLAStaticScratch(self._op, _stream(self.device, stream))
+        _check(st, "mpaMLAStaticScratch")
+        return (self.out, self.lse) if self.lse is not None else self.out
+
     def set_launch_events(self, start=None, stop=None):
         """Later runs record ``start`` at the split kernel's start and ``stop`` at the
         end of the call's last kernel (torch.cuda.Event with timing, created, or None)."""

@@ -58,6 +58,7 @@ SIGNATURES = {
         ctypes.c_int, ctypes.c_int64,                # dtype, nTokens
         c_vp, c_vp, c_u64p, c_opp]),                 # attenOut, lse, workspaceSize, op
     "mpaMLA": (ctypes.c_int32, [c_vp, ctypes.c_uint64, c_vp, c_vp]),
+    "mpaMLAStaticScratch": (ctypes.c_int32, [c_vp, c_vp]),
     "mpaLseMerge": (ctypes.c_int32, [
         c_vp, c_vp, ctypes.c_int32, ctypes.c_int64,  # oParts, lseParts, nParts, rows
         ctypes.c_int32, ctypes.c_int, c_vp, c_vp, c_vp]),  # headDim, dtype, out, lse, stream

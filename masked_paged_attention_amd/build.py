@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmpa.so")
 
-SOURCES = ["api.cpp", "planner.cpp", "prefill_fwd.hip", "mla_decode.hip", "lse_merge.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "prefill_fwd.hip", "mla_decode.hip", "lse_merge.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 

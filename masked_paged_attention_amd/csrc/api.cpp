@@ -51,6 +51,7 @@ int shift_of(int bs) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+static_assert(MPA_MLA_STATIC_SCRATCH_BYTES == mpa::kStaticScratchBytes, "static scratch size");
 // kernel mask type of the chunked local causal mask (selected through the
 // chunked entry point; not a PrefixEncoder maskType value)
 constexpr int kMaskChunkedCausal = 10;
@@ -537,9 +538,10 @@ mpaStatus mpaMLAInt8GetWorkspaceSize(const void* qNope, const void* qRope, const
                      pvDescale);
 }
 
-mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void* stream) {
-  g_last_error.clear();
-  if (!op || op->kind != mpaOperation::kMla) return fail(MPA_ERROR_INVALID_ARG, "op is not an MLA operation");
+namespace {
+
+// Execution of an MLA operation with its plan and partials in `workspace`.
+mpaStatus run_mla(mpaOperation* op, void* workspace, uint64_t workspaceSize, void* stream) {
   mpaStatus st = bind_workspace(op, workspace, workspaceSize, (hipStream_t)stream);
   if (st != MPA_OK) return st;
   mpa::MlaParams p = op->mp;
@@ -553,6 +555,29 @@ mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void
   hipError_t e = mpa::launch_mla(p, op->dtype, (hipStream_t)stream, op->events);
   if (e != hipSuccess) return hip_fail(e, "MLA launch");
   return MPA_OK;
+}
+
+}  // namespace
+
+mpaStatus mpaMLA(void* workspace, uint64_t workspaceSize, mpaOperation* op, void* stream) {
+  g_last_error.clear();
+  if (!op || op->kind != mpaOperation::kMla) return fail(MPA_ERROR_INVALID_ARG, "op is not an MLA operation");
+  return run_mla(op, workspace, workspaceSize, stream);
+}
+
+mpaStatus mpaMLAStaticScratch(mpaOperation* op, void* stream) {
+  g_last_error.clear();
+  if (!op || op->kind != mpaOperation::kMla) return fail(MPA_ERROR_INVALID_ARG, "op is not an MLA operation");
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  hipError_t e = mpa::static_scratch(&scratch, &bytes);
+  if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+  if (op->ws_bytes > bytes)
+    return fail(MPA_ERROR_WORKSPACE_TOO_SMALL,
+                "the operation needs %llu bytes of scratch; the static scratch holds %llu (use mpaMLA with a "
+                "workspace)",
+                (unsigned long long)op->ws_bytes, (unsigned long long)bytes);
+  return run_mla(op, scratch, bytes, stream);
 }
 
 mpaStatus mpaLseMerge(const void* oParts, const float* lseParts, int32_t nParts, int64_t rows,

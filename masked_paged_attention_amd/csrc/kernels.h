@@ -92,4 +92,11 @@ struct LseMergeParams {
 
 hipError_t launch_lse_merge(const LseMergeParams& p, int dtype, hipStream_t stream);
 
+// Bytes of the library-owned device buffer behind mpaMLAStaticScratch (per GPU).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+// Device address (on the current device) and size of that buffer; looked up
+// once per device.
+hipError_t static_scratch(void** ptr, size_t* bytes);
+
 }  // namespace mpa

@@ -14,5 +14,6 @@ hipError_t launch_prefill(const PrefillParams&, int, int, int, int, hipStream_t,
 }
 hipError_t launch_mla(const MlaParams&, int, hipStream_t, const LaunchEvents&) { return hipErrorNoDevice; }
 hipError_t launch_lse_merge(const LseMergeParams&, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t static_scratch(void**, size_t*) { return hipErrorNoDevice; }
 
 }  // namespace mpa

@@ -53,6 +53,7 @@ constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
+constexpr int kSqrtFar = 384;  // sqrt ALiBi: distance from which a tile's bias is expanded
 
 template <typename T, int D, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
@@ -574,9 +575,30 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   float m_run = -INFINITY;
   float l_run = 0.0f;
   const int a_lane = prefix + wrow0 + lq;
+  const int a_lane0 = prefix + wrow0;  // the wave's first row
   float slope2 = 0.0f;
   if constexpr (kAlibiLinear || kAlibiSqrt || kTileAlibi) slope2 = p.slopes[head] * kLog2e;
-  const float scale2 = p.scale2;
+  float scale2 = p.scale2;
+  // Linear ALiBi: the S^T accumulator of every key tile starts at slope2 C /
+  // scale2 for its key C (the same for every lane and tile), so that the score
+  // S^T scale2 + (-slope2 dbase - m) is one FMA.  Below |scale2| = 2^-100, where
+  // slope2 / scale2 could overflow, the q.k part (at most 2^-100 |q.k|, under
+  // 2^-60 for fp16 inputs and for bf16 inputs below 2^16) is dropped: Q is zeroed
+  // and the scale taken as 1.
+  f32x16 binit[2];
+  if constexpr (kAlibiLinear) {
+    if (!(__builtin_fabsf(scale2) >= 0x1p-100f)) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qreg[c] = V8{};
+      scale2 = 1.0f;
+    }
+    const float c2 = slope2 / scale2;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) binit[kb][r] = c2 * (float)(32 * kb + 8 * (r >> 2) + (r & 3));
+    }
+  }
 
   // Compressed tile entries of this lane's query row for a key tile that needs
   // them: 8 runs of 4 (the tile's 64 columns) from row r = a mod 128 (the key in
@@ -633,7 +655,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     auto score = [&](int kb, int r, float m_ref, float nbm, bool checked) __attribute__((always_inline)) -> float {
       const int C = 32 * kb + 8 * (r >> 2) + (r & 3);
       if constexpr (kAlibiLinear) {
-        return __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(slope2, (float)C, nbm));
+        (void)C;
+        return __builtin_fmaf(s[kb][r], scale2, nbm);  // slope2 C is in S^T (binit)
       } else if constexpr (kAlibiSqrt) {
         return __builtin_fmaf(-slope2, fast_sqrt(dbf - (float)C), __builtin_fmaf(s[kb][r], scale2, -m_ref));
       } else if constexpr (kTileAlibi) {
@@ -655,14 +678,44 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     if (kReverse && !partial && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
       const float nbm = -slope2 * dbf - m_run;
       float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // Sqrt ALiBi on a tile whose every distance is >= kSqrtFar: the bias of
+      // each 32-key half from a quadratic expansion of -slope2 sqrt(d) around
+      // the half's centre (a lane's keys C = 32kb + 0..27, centre 32kb + 13.5):
+      // one square root per half instead of one per score; |error| <=
+      // 13.5^3 / (16 kSqrtFar^2.5) = 5.3e-5 in units of sqrt(d), times slope2.
+      auto fast = [&](auto FAR) __attribute__((always_inline)) {
+        float b0[2], b1[2], b2[2];
+        if constexpr (decltype(FAR)::value) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(score(kb, r, m_run, nbm, false));
-          x[kb][r] = e;
-          ps[r & 3] += e;
+          for (int kb = 0; kb < 2; ++kb) {
+            const float d0 = dbf - (32.0f * kb + 13.5f);
+            const float rs = __builtin_amdgcn_rsqf(d0);
+            b0[kb] = -slope2 * d0 * rs - m_run;  // -slope2 sqrt(d0), relative to m_run
+            b1[kb] = 0.5f * slope2 * rs;         // first-order term (d falls as C grows)
+            b2[kb] = 0.25f * b1[kb] * rs * rs;   // second-order term, slope2 / (8 d0^1.5)
+          }
         }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float sc;
+            if constexpr (decltype(FAR)::value) {
+              const float dl = (float)(8 * (r >> 2) + (r & 3)) - 13.5f;
+              sc = __builtin_fmaf(s[kb][r], scale2, __builtin_fmaf(__builtin_fmaf(b2[kb], dl, b1[kb]), dl, b0[kb]));
+            } else {
+              sc = score(kb, r, m_run, nbm, false);
+            }
+            const float e = fast_exp2(sc);
+            x[kb][r] = e;
+            ps[r & 3] += e;
+          }
+        }
+      };
+      if (kAlibiSqrt && a_lane0 - t * kBN - (kBN - 1) >= kSqrtFar) {
+        fast(std::true_type{});
+      } else {
+        fast(std::false_type{});
       }
       psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
       done = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) == 0;
@@ -777,8 +830,13 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
         // issued below: only the tiles from the first row's block on)
         if (needs_tile_mask(t)) load_tile_mask(t);
       }
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+      if constexpr (kAlibiLinear) {
+        s[0] = binit[0];
+        s[1] = binit[1];
+      } else {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+      }
       // K operand reads run kQkDepth MFMAs ahead; the next tile's loads sit
       // between the MFMAs in one straight-line version (no branch between them)
       // and are left out of the other (last iteration).

@@ -860,6 +860,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           __builtin_amdgcn_sched_barrier(0);
         }
       };
+      // Wave priority 2 for the matrix phases, 0 for the softmax: of the two
+      // waves sharing a SIMD, one in its softmax yields issue slots to one
+      // feeding the matrix cores, which spreads the two waves' phases apart.
+      __builtin_amdgcn_s_setprio(2);
       if (load_next) {
         qk(std::true_type{});
       } else {
@@ -867,7 +871,9 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       }
       // block id two iterations ahead, read while the softmax runs
       blk_next = block_of(u + 2);
+      __builtin_amdgcn_s_setprio(0);
       softmax(t);
+      __builtin_amdgcn_s_setprio(2);
       // the next key tile's ALiBi tile entries (this tile's are consumed)
       if constexpr (kTileAlibi) {
         if (u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));

@@ -228,7 +228,8 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void *workspace, uint64_t workspaceSize,
  *   attenOut   dev [T, headNum, 512] dtype (output)
  *   lse        dev [T, headNum] fp32 natural-log LSE (output), or NULL
  *   workspaceSize, op  outputs: device workspace bytes (the launch plan, then
- *              the split-KV partial results) and the new operation
+ *              the split-KV partial results, kept in fp32 with their fp32 LSE
+ *              so that the merge rounds to dtype once) and the new operation
  */
 mpaStatus mpaMLAGetWorkspaceSize(
     const void *qNope, const void *qRope, const void *ctKV, const void *kRope,
@@ -274,7 +275,7 @@ mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid it).  The same launches as mpaMLA, with the plan and the split-KV
  * partials in a buffer the library owns: a static device array of
- * MPA_MLA_STATIC_SCRATCH_BYTES bytes (64 MiB), one per GPU, held until the
+ * MPA_MLA_STATIC_SCRATCH_BYTES bytes (128 MiB), one per GPU, held until the
  * process ends.  Nothing is allocated and nothing must be zeroed: every
  * execution first copies its plan into the buffer and writes every partial it
  * reads.  All executions on one GPU share that GPU's buffer: executions that
@@ -286,7 +287,7 @@ mpaStatus mpaMLA(void *workspace, uint64_t workspaceSize, mpaOperation *op, void
  * Errors: MPA_ERROR_INVALID_ARG (op NULL or not MLA), MPA_ERROR_WORKSPACE_TOO_SMALL
  * (the operation needs more than the static buffer: use mpaMLA), MPA_ERROR_HIP.
  */
-#define MPA_MLA_STATIC_SCRATCH_BYTES (64ull << 20)
+#define MPA_MLA_STATIC_SCRATCH_BYTES (128ull << 20)
 mpaStatus mpaMLAStaticScratch(mpaOperation *op, void *stream);
 
 /*

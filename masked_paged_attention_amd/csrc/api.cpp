@@ -498,7 +498,7 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   p.pv_descale = pvDescale;
   // workspace: plan, partial outputs (input type), partial LSEs (fp32)
   o->part_o_off = o->plan_bytes;
-  o->part_lse_off = o->part_o_off + align_up((uint64_t)plan.part_rows * 512 * 2);
+  o->part_lse_off = o->part_o_off + align_up((uint64_t)plan.part_rows * 512 * 4);  // fp32 partials
   o->ws_bytes = o->part_lse_off + align_up((uint64_t)plan.part_rows * 4);
   *workspaceSize = o->ws_bytes;
   *op = o;

@@ -56,7 +56,7 @@ struct MlaParams {
   const int32_t* piece_seg;    // piece p: segments [piece_seg[p], piece_seg[p + 1])
   const int4* seqs;            // per sequence: {ctx, q_len, tok0, n_parts}
   const int4* seqs2;           // per sequence: {part_row0, rows (q_len * H), 0, 0}
-  void* part_o;                // [part_rows, 512] partial outputs (input type) in the workspace
+  void* part_o;                // [part_rows, 512] fp32 partial outputs in the workspace
   float* part_lse;             // [part_rows] fp32 log2-domain LSE in the workspace
   void* out;                   // [T, H, 512]
   float* lse;                  // [T, H] or null
@@ -93,7 +93,7 @@ struct LseMergeParams {
 hipError_t launch_lse_merge(const LseMergeParams& p, int dtype, hipStream_t stream);
 
 // Bytes of the library-owned device buffer behind mpaMLAStaticScratch (per GPU).
-constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
 
 // Device address (on the current device) and size of that buffer; looked up
 // once per device.

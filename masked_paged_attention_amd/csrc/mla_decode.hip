@@ -568,24 +568,36 @@ __global__ void __launch_bounds__(512, 1)
     const int gl = ln >> 5;
     const float inv = (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) * (Q8 ? pv_desc : 1.0f);
     const float lse2 = l_tot > 0.0f ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
-    T* orow;
     if (sg.w < 0) {
-      orow = (T*)p.out + ((long long)sq.z * H + mr) * kDv;
+      T* orow = (T*)p.out + ((long long)sq.z * H + mr) * kDv + 256 * hf + 4 * gl;
       if (p.lse != nullptr && gl == 0 && hf == 0) p.lse[(long long)sq.z * H + mr] = lse2 * kLn2;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typename Vec<T>::x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (T)((o[dt][4 * q + e] - bias) * inv);
+          *(typename Vec<T>::x4*)(orow + 32 * dt + 8 * q) = v;
+        }
+      }
     } else {
+      // A partial result stays in fp32: the merge rounds the sum to the output
+      // type once, so that the split adds no rounding of its own.
       const long long prow = (long long)sq2.x + (long long)sg.w * sq2.y + mr;
-      orow = (T*)p.part_o + prow * kDv;
+      float* orow = (float*)p.part_o + prow * kDv + 256 * hf + 4 * gl;
       if (gl == 0 && hf == 0) p.part_lse[prow] = lse2;
-    }
-    orow += 256 * hf + 4 * gl;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+      for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        typename Vec<T>::x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (T)((o[dt][4 * q + e] - bias) * inv);
-        *(typename Vec<T>::x4*)(orow + 32 * dt + 8 * q) = v;
+        for (int q = 0; q < 4; ++q) {
+          float4 v;
+          v.x = (o[dt][4 * q + 0] - bias) * inv;
+          v.y = (o[dt][4 * q + 1] - bias) * inv;
+          v.z = (o[dt][4 * q + 2] - bias) * inv;
+          v.w = (o[dt][4 * q + 3] - bias) * inv;
+          *(float4*)(orow + 32 * dt + 8 * q) = v;
+        }
       }
     }
   };
@@ -683,18 +695,20 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float tot = 0.0f;
   for (int k0 = 0; k0 < n; k0 += 8) {
-    typename Vec<T>::x8 a[8];
+    float4 a[8][2];
     float wgt[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u < n) {
         const long long row = base + (long long)(k0 + u) * rows;
         wgt[u] = p.part_lse[row];
-        a[u] = *(const typename Vec<T>::x8*)((const T*)p.part_o + row * kDv + 8 * l);
+        const float4* src = (const float4*)((const float*)p.part_o + row * kDv + 8 * l);
+        a[u][0] = src[0];
+        a[u][1] = src[1];
       } else {
         wgt[u] = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[u][e] = (T)0.0f;
+        a[u][0] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        a[u][1] = float4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
     float gm = mref;
@@ -710,8 +724,14 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
       if (wgt[u] == -INFINITY) continue;  // an empty part: its values stay out of the sum
       const float wu = fast_exp2(wgt[u] - gm);
       tot += wu;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wu * (float)a[u][e];
+      acc[0] += wu * a[u][0].x;
+      acc[1] += wu * a[u][0].y;
+      acc[2] += wu * a[u][0].z;
+      acc[3] += wu * a[u][0].w;
+      acc[4] += wu * a[u][1].x;
+      acc[5] += wu * a[u][1].y;
+      acc[6] += wu * a[u][1].z;
+      acc[7] += wu * a[u][1].w;
     }
     mref = gm;
   }

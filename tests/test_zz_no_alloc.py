@@ -15,7 +15,7 @@ from gpu_helpers import check_mla, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-STATIC_BYTES = 64 << 20
+STATIC_BYTES = 128 << 20
 
 
 def _pair(case):
@@ -60,7 +60,7 @@ def test_static_scratch_refuses_an_operation_that_does_not_fit():
     import masked_paged_attention_amd as mpa
     log("case static scratch: an operation larger than the buffer")
     # one sequence of 128 new tokens: 16384 (token, head) rows, split over 8
-    # pieces of its keys -- 131072 partial rows (~134 MB)
+    # pieces of its keys -- 131072 fp32 partial rows (~268 MB)
     ctx = np.array([4096], dtype=np.int32)
     ql = np.array([128], dtype=np.int32)
     c = W.make_mla(503, ctx, ql, 128, 128, "bf16", 1, 1, 1, 1.0 / np.sqrt(192.0), name="big-spec").to(DEV)

@@ -368,6 +368,46 @@ def cpu_baseline(case, name, max_workers=16, max_pairs=40):
             "seconds": round(dt, 2), "valid_flops": int(flops)}
 
 
+def measure_peaks(torch, command, iters=20):
+    """Achievable rates of the GPU, as context for the published peaks the roofline
+    uses: a 1 GiB device-to-device copy (HBM read + write) and an 8192^3 bf16
+    GEMM through torch (the vendor BLAS), each timed with events over `iters`
+    calls after a warm-up."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lines = [f"command: {command}" if command else "command: python bench.py --peaks",
+             f"device: {torch.cuda.get_device_name(dev)}"]
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        a, b = _events(torch)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    ms = timed(lambda: dst.copy_(src))
+    gbs = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    lines.append(f"copy 1 GiB -> 1 GiB: {ms:.4f} ms per copy, {gbs:.1f} GB/s read + write "
+                 f"({gbs / 8000:.3f} of 8 TB/s)")
+    del src, dst
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(5)
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev, generator=g)
+    ms = timed(lambda: torch.matmul(a, b))
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    lines.append(f"bf16 GEMM {n}x{n}x{n} (torch.matmul): {ms:.4f} ms, {tf:.1f} TFLOP/s "
+                 f"({tf / 2500:.3f} of 2.5 PFLOP/s dense)")
+    return "\n".join(lines) + "\n"
+
+
 def _sum_or_none(*xs):
     return None if any(x is None for x in xs) else int(sum(xs))
 
@@ -393,6 +433,8 @@ def main():
     ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
                     help="print per-kernel means of a rocprofv3 --pmc counter_collection.csv and exit")
     ap.add_argument("--command", default="", help="the profiling command(s), recorded in a summary")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the achievable HBM copy rate and bf16 GEMM rate of the GPU and exit")
     args = ap.parse_args()
     if args.summarize_stats:
         sys.stdout.write(summarize_kernel_stats(args.summarize_stats, args.command))
@@ -410,6 +452,10 @@ def main():
 
     import torch
     import workloads as W
+
+    if args.peaks:
+        sys.stdout.write(measure_peaks(torch, args.command))
+        return
 
     # Inputs of the headline prefill workload, generated on the host; the CPU
     # baseline runs the oracle on them before anything touches the GPU (its

@@ -354,6 +354,15 @@ def test_compressed_mask_validation(lib, kw, status):
     assert lib.mpaGetLastErrorMessage()
 
 
+def test_compressed_mask_head_seq_form_is_refused_by_name(lib):
+    # the [headNum, seqLen, 128] ALiBi form is out of scope: refused as unsupported,
+    # with a message that names the form, before anything else happens
+    st, op = _prefill_tile(lib, mask=4, slopes=FAKE, rows=256, cols=128)
+    assert st == 2
+    assert b"[headNum, seqLen, 128]" in lib.mpaGetLastErrorMessage()
+    assert op.value is None or op.value == 0
+
+
 def test_compressed_mask_valid_args_reach_hip_or_succeed(lib):
     for kw in (dict(), dict(mask=4, slopes=FAKE, rows=256, cols=256)):
         st, op = _prefill_tile(lib, **kw)

@@ -878,15 +878,24 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       if constexpr (kTileAlibi) {
         if (u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));
       }
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+      {
+        auto rv = [&](int i) -> V8 {
+          const int kc = i / NDT, dt = i % NDT;
           const char* src = lds + kB + va[dt] + 4160 * kc;
           const s16x4 lo = lds_read_tr16((const T*)src);
           const s16x4 hi = lds_read_tr16((const T*)(src + 2080));
-          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = mfma32(__builtin_bit_cast(V8, both), pk[kc], o[dt]);
+          return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr int kPvDepth = 3;
+        V8 vring[kPvDepth];
+#pragma unroll
+        for (int i = 0; i < kPvDepth; ++i) vring[i] = rv(i);
+#pragma unroll
+        for (int i = 0; i < 4 * NDT; ++i) {
+          const V8 a = vring[i % kPvDepth];
+          if (i + kPvDepth < 4 * NDT) vring[i % kPvDepth] = rv(i + kPvDepth);
+          o[i % NDT] = mfma32(a, pk[i / NDT], o[i % NDT]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {

@@ -171,6 +171,19 @@ def test_packed_equals_padded_full_size():
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("mask", [3, 5])
+@pytest.mark.parametrize("scale", [0.0, 1e-35, -1.0 / np.sqrt(128)])
+def test_linear_alibi_zero_tiny_and_negative_scales(dtype, mask, scale):
+    # The linear-ALiBi kernel (headSize 128, blockSize 128) starts each tile's S^T
+    # accumulator at slope*C/qkScale; at qkScale 0 and below 2^-100 it drops the
+    # q.k part instead, and a negative qkScale flips that start's sign.
+    log(f"case linear ALiBi dtype={dtype} mask={mask} qkScale={scale}")
+    c = _case(420 + mask, [300, 129, 70], [200, 0, 520], 4, 2, 128, 128, dtype, mask, scale=scale)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("mask", [3, 4, 5])
 def test_alibi_score_spikes_move_the_running_max(dtype, mask):
     # Keys far from the diagonal with very large dot products: visiting tiles from

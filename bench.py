@@ -525,12 +525,18 @@ def main():
 
     # The GPU leaves its idle clocks over the first few tens of milliseconds of
     # work (the first calls of a fresh process run up to 3x slower): the step runs
-    # untimed for PREWARM_S seconds before the W warm-up steps.
+    # untimed, back to back, for about PREWARM_S seconds before the W warm-up
+    # steps.  (With a synchronisation after every pre-warm step instead, the
+    # first one or two timed launches of one call still took ~3x their steady
+    # time.)
     print("bench: clock pre-warm + warmup", file=sys.stderr, flush=True)
     t_pw = time.perf_counter()
-    while time.perf_counter() - t_pw < PREWARM_S:
-        step(0)
-        torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    t_one = max(time.perf_counter() - t_pw, 1e-3)
+    for i in range(max(1, int(PREWARM_S / t_one))):
+        step(i)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -543,9 +549,16 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    sq_ms = float(np.mean([e[0][0].elapsed_time(e[0][1]) for e in evs]))
-    lf_ms = float(np.mean([e[1][0].elapsed_time(e[1][1]) for e in evs]))
-    m_ms = float(np.mean([e[2][0].elapsed_time(e[2][1]) for e in evs]))
+    sq_all = [e[0][0].elapsed_time(e[0][1]) for e in evs]
+    lf_all = [e[1][0].elapsed_time(e[1][1]) for e in evs]
+    m_all = [e[2][0].elapsed_time(e[2][1]) for e in evs]
+    sq_ms, lf_ms, m_ms = float(np.mean(sq_all)), float(np.mean(lf_all)), float(np.mean(m_all))
+
+    def spread(ts):
+        # the spread of one call's launches over the timed steps (the rates above
+        # use the mean of all of them)
+        return {"ms_median": round(float(np.median(ts)), 5), "ms_min": round(float(np.min(ts)), 5),
+                "ms_max": round(float(np.max(ts)), 5)}
     for op in p_ops + m_ops:
         op.set_launch_events(None, None)
     p_tflops = 2 * p_flops / ((sq_ms + lf_ms) * 1e-3) / 1e12
@@ -710,13 +723,13 @@ def main():
                      "per_launch_flops": int(p_flops), "ms": round(dom_ms, 5)},
         "prefill": {"sqrt": {"ms": round(sq_ms, 5), "tflops": round(sq_tf, 1),
                              "frac_mfma": round(sq_tf / PEAK_MFMA_TFLOPS, 4),
-                             "traffic": read_traffic("prefill_dma_kernel<bf16,4>")},
+                             "traffic": read_traffic("prefill_dma_kernel<bf16,4>"), **spread(sq_all)},
                     "left": {"ms": round(lf_ms, 5), "tflops": round(lf_tf, 1),
                              "frac_mfma": round(lf_tf / PEAK_MFMA_TFLOPS, 4),
-                             "traffic": read_traffic("prefill_dma_kernel<bf16,5>")},
+                             "traffic": read_traffic("prefill_dma_kernel<bf16,5>"), **spread(lf_all)},
                     "target": "50% of dense bf16 MFMA peak (<= 2.2 ms per call)"},
         "decode": {"value": round(m_gbs, 1), "unit": "GB/s", "frac_hbm": round(m_gbs / PEAK_HBM_GBS, 4),
-                   "ms": round(m_ms, 5), "bytes": int(m_bytes),
+                   "ms": round(m_ms, 5), "bytes": int(m_bytes), **spread(m_all),
                    "tflops": round(m_flops / (m_ms * 1e-3) / 1e12, 1),
                    "traffic": _sum_or_none(read_traffic("mla_split_kernel"), read_traffic("mla_combine_kernel")),
                    "target": "70% of HBM",

@@ -295,11 +295,15 @@ def time_ops(torch, ops, iters, warmup):
     """Average ms of one call over iters back-to-back calls of the operations in turn,
     from events recorded on each call's own kernels (its first kernel's start, its
     last kernel's end: mpaOperationSetLaunchEvents), so no command sits between the
-    calls on the stream."""
-    for i in range(warmup):
-        ops[i % len(ops)].run()
-    torch.cuda.synchronize()
+    calls on the stream.  The warm-up calls carry the same events: the first
+    launch that records a given event that way runs several times slower, and
+    must not be a timed one."""
     evs = launch_events(torch, iters)
+    for i in range(max(warmup, iters)):
+        op = ops[i % len(ops)]
+        op.set_launch_events(*evs[i % iters])
+        op.run()
+    torch.cuda.synchronize()
     for i, (a, b) in enumerate(evs):
         op = ops[i % len(ops)]
         op.set_launch_events(a, b)
@@ -526,22 +530,24 @@ def main():
     # The GPU leaves its idle clocks over the first few tens of milliseconds of
     # work (the first calls of a fresh process run up to 3x slower): the step runs
     # untimed, back to back, for about PREWARM_S seconds before the W warm-up
-    # steps.  (With a synchronisation after every pre-warm step instead, the
-    # first one or two timed launches of one call still took ~3x their steady
-    # time.)
+    # steps.
     print("bench: clock pre-warm + warmup", file=sys.stderr, flush=True)
+    # (the timing events exist before the warm-up: creating them between the
+    # warm-up and the timed steps would leave the GPU idle there)
+    evs = [launch_events(torch, 3) for _ in range(args.steps)]
+    t_start, t_end = _events(torch)
     t_pw = time.perf_counter()
     step(0)
     torch.cuda.synchronize()
     t_one = max(time.perf_counter() - t_pw, 1e-3)
+    # (the untimed steps carry the timed steps' events: the first launch that
+    # records a given event on its kernel runs several times slower, and must
+    # not be a timed one)
     for i in range(max(1, int(PREWARM_S / t_one))):
-        step(i)
+        step(i, evs[i % args.steps])
     torch.cuda.synchronize()
     for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [launch_events(torch, 3) for _ in range(args.steps)]
-    t_start, t_end = _events(torch)
+        step(i, evs[i % args.steps])
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):

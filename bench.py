@@ -167,8 +167,11 @@ def short_kernel_name(mangled):
     return mangled
 
 
-def summarize_kernel_stats(stats_csv, command):
-    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+def summarize_kernel_stats(stats_csv, command, last=0):
+    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv; with
+    last > 0 also the mean duration of each kernel's last `last` dispatches, from
+    the kernel_trace.csv beside it (the timed steps of a bench run: the earlier
+    dispatches include the untimed pre-warm and warm-up)."""
     rows = list(csv.DictReader(open(stats_csv)))
     out = ["# rocprofv3 kernel statistics", "# command:", "#   " + command,
            f"# kernel sources digest: {kernel_source_digest()}", "",
@@ -177,6 +180,17 @@ def summarize_kernel_stats(stats_csv, command):
         out.append(f"{short_kernel_name(r['Name']):44s} {int(r['Calls']):6d} "
                    f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
                    f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):7.2f}")
+    trace_csv = stats_csv.replace("kernel_stats.csv", "kernel_trace.csv")
+    if last > 0 and os.path.exists(trace_csv):
+        per = {}
+        for r in csv.DictReader(open(trace_csv)):
+            per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        out += ["", f"# mean of each kernel's last {last} dispatches (in launch order)",
+                f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s}"]
+        for k, v in per.items():
+            d = [x[1] for x in sorted(v)[-last:]]
+            out.append(f"{k:44s} {len(d):6d} {float(np.mean(d)) / 1e3:10.2f}")
     return "\n".join(out) + "\n"
 
 
@@ -432,6 +446,8 @@ def main():
                     help="run one 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 kernel_stats.csv and exit")
+    ap.add_argument("--last", type=int, default=0,
+                    help="with --summarize-stats: also the mean of each kernel's last N dispatches")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print HBM bytes per dispatch from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
@@ -441,7 +457,7 @@ def main():
                     help="measure the achievable HBM copy rate and bf16 GEMM rate of the GPU and exit")
     args = ap.parse_args()
     if args.summarize_stats:
-        sys.stdout.write(summarize_kernel_stats(args.summarize_stats, args.command))
+        sys.stdout.write(summarize_kernel_stats(args.summarize_stats, args.command, args.last))
         return
     if args.summarize_traffic:
         sys.stdout.write(summarize_traffic(*args.summarize_traffic, args.command))

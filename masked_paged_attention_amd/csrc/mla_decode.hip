@@ -24,8 +24,7 @@
 // is rescaled only when a row's max grows by more than 2^8 (exact: the final
 // normalisation uses the same reference max).  A segment that covers its whole
 // sequence writes the final output; the others write a normalised partial
-// output (rounded to the input type) and a log2-domain LSE (fp32) to the
-// workspace.
+// output and a log2-domain LSE, both fp32, to the workspace.
 //
 // Kernel 2 (combine): for each (token, head) of a sequence with several
 // segments, LSE-weighted merge of the partials: L = log2 sum_s 2^{lse_s}, out = sum_s 2^{lse_s - L} o_s --

@@ -99,3 +99,61 @@ def test_chunked_valid_flops_match_brute_force():
             a = k_ - l_ + i
             pairs += sum(1 for j in range(k_) if j <= a and j // C == a // C)
     assert bench.prefill_valid_flops_chunked(L, kv, C, 3, 64) == pairs * 3 * 4 * 64
+
+
+class _FakeEvent:
+    def __init__(self, log):
+        self.log = log
+
+    def record(self):
+        pass
+
+    def elapsed_time(self, other):
+        return 1.0
+
+
+class _FakeCuda:
+    def __init__(self, log):
+        self.log = log
+
+    def Event(self, enable_timing=True):
+        return _FakeEvent(self.log)
+
+    def synchronize(self):
+        self.log.append(("sync",))
+
+
+class _FakeTorch:
+    def __init__(self, log):
+        self.cuda = _FakeCuda(log)
+
+
+class _FakeOp:
+    def __init__(self, log):
+        self.log = log
+        self.ev = None
+
+    def set_launch_events(self, a, b):
+        self.ev = (a, b)
+
+    def run(self):
+        self.log.append(("run", self.ev))
+
+
+@pytest.mark.parametrize("iters,warmup", [(10, 3), (20, 4), (4, 9)])
+def test_every_timing_event_is_used_once_before_its_timed_launch(iters, warmup):
+    # a launch that records an event on its kernels for the first time runs
+    # several times slower: time_ops must give every event pair an untimed launch
+    # first, and time exactly `iters` launches after the last synchronisation
+    log = []
+    ops = [_FakeOp(log), _FakeOp(log)]
+    ms = bench.time_ops(_FakeTorch(log), ops, iters, warmup)
+    assert ms == 1.0
+    syncs = [i for i, e in enumerate(log) if e[0] == "sync"]
+    runs = [(i, e[1]) for i, e in enumerate(log) if e[0] == "run"]
+    timed = [ev for i, ev in runs if syncs[-2] < i < syncs[-1]]
+    untimed = [ev for i, ev in runs if i < syncs[-2]]
+    assert len(timed) == iters and all(ev is not None for ev in timed)
+    assert len(untimed) >= max(warmup, iters)
+    warmed = {(id(a), id(b)) for a, b in untimed if a is not None}
+    assert all((id(a), id(b)) in warmed for a, b in timed)

@@ -167,6 +167,7 @@ __global__ void __launch_bounds__(512, 1)
   auto tile_block = [&]() -> int {
     return ONE_BLOCK ? block_tables[(long long)lb * p.max_blocks + (lj >> p.bs_shift)] : 0;
   };
+
   auto ld_advance = [&]() {
     lj += kBN;
     if (lj >= lk1) {
@@ -176,6 +177,16 @@ __global__ void __launch_bounds__(512, 1)
         lb = sg.x; lj = sg.y; lk1 = sg.z;
       }
     }
+  };
+  // A tile whose loads are due: its block id (one-block tiles) and the loader
+  // cursor at it (sequence, first key, segment end); the cursor moves on.
+  struct TileRef {
+    int blk, b, j, k1;
+  };
+  auto take_tile = [&]() -> TileRef {
+    const TileRef r{tile_block(), lb, lj, lk1};
+    ld_advance();
+    return r;
   };
   // Row r of the cache: latent at lat_row(r), rope at rope_row(r).
   const bool split_rope = p.krope != nullptr;
@@ -190,8 +201,9 @@ __global__ void __launch_bounds__(512, 1)
   // (finite data, masked later).
   const long long lat_step = (long long)p.ckv_stride * (long long)sizeof(T);
   const long long rope_step = split_rope ? 64 * (long long)sizeof(T) : lat_step;
-  auto issue = [&](int blk, T* buf) __attribute__((always_inline)) {
-    const int last = lk1 - 1 - lj;  // last key of the segment within the tile
+  auto issue = [&](const TileRef& tr, T* buf) __attribute__((always_inline)) {
+    const int blk = tr.blk, lj = tr.j;
+    const int last = tr.k1 - 1 - lj;  // last key of the segment within the tile
     const unsigned m0buf = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)buf;
     if constexpr (Q8) {
       // Latent: wave w fills slots 4w .. 4w+3 and the same + 16 (lanes 32..63),
@@ -213,7 +225,7 @@ __global__ void __launch_bounds__(512, 1)
                (unsigned)min(ropekey, last) * 64u * (unsigned)sizeof(T) + ropecol,
                buf + kLatElems + 64 * 8 * w);
       } else {
-        const int32_t* bt = block_tables + (long long)lb * p.max_blocks;
+        const int32_t* bt = block_tables + (long long)tr.b * p.max_blocks;
         auto row_of = [&](int key) -> long long {
           const int j = lj + min(key, last);
           const int bi = j / p.block_size;
@@ -246,7 +258,7 @@ __global__ void __launch_bounds__(512, 1)
                            16u * (unsigned)((ln & 7) ^ rope_swz(key));
       dma16s(rope_row(rt), off, buf + kLatElems + 64 * 8 * w);
     } else {
-      const int32_t* bt = block_tables + (long long)lb * p.max_blocks;
+      const int32_t* bt = block_tables + (long long)tr.b * p.max_blocks;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int j = lj + min(8 * w + k, last);
@@ -618,15 +630,9 @@ __global__ void __launch_bounds__(512, 1)
 
   // ---- prologue: loads of the first two tiles, queries of the first segment ----
   const bool loader = w < 4;
-  int blk_next = 0;
   if (loader) {
-    issue(tile_block(), tbuf);
-    ld_advance();
-    if (n_total > 1) {
-      issue(tile_block(), tbuf + kBufElems);
-      ld_advance();
-    }
-    if (n_total > 2) blk_next = tile_block();
+    issue(take_tile(), tbuf);
+    if (n_total > 1) issue(take_tile(), tbuf + kBufElems);
   }
   load_q(cs);
   reset_state(cs);
@@ -655,12 +661,16 @@ __global__ void __launch_bounds__(512, 1)
       const int nxt = next_valid(cs + 1);
       if (nxt < s_end) load_q(nxt);
     }
+    // The scalar reads behind tile t+2's loads (its block id; plan records
+    // when the cursor enters the next segment) go here, where the wave is about
+    // to wait for its partner anyway: scalar loads and LDS reads share one
+    // counter, and scalar loads complete out of order, so any LDS wait behind a
+    // scalar load in flight waits for that load too.
+    TileRef nx{};
+    const bool load_next = loader && t + 2 < n_total;
+    if (load_next) nx = take_tile();
     lds_barrier();  // exchange slots written; the direct loads in flight stay in flight
-    if (loader && t + 2 < n_total) {
-      issue(blk_next, tbuf + ((t + 2) % 3) * kBufElems);
-      ld_advance();
-      if (t + 3 < n_total) blk_next = tile_block();
-    }
+    if (load_next) issue(nx, tbuf + ((t + 2) % 3) * kBufElems);
     smpv_part(cur);
     const int done = cs;
     if (advance_cursor()) {

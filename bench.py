@@ -236,15 +236,26 @@ def summarize_traffic(fetch_csv, write_csv, command, copy_bytes=1 << 30):
     return "\n".join(out) + "\n"
 
 
+XCDS = 8  # accelerator complex dies of an MI355X, each with its own GRBM_GUI_ACTIVE
+
+
 def summarize_counters(pmc_csv, command):
     """Per-kernel means over dispatches of every counter in a rocprofv3 --pmc
-    counter_collection.csv (device copies left out)."""
+    counter_collection.csv (device copies left out).  With GRBM_GUI_ACTIVE among
+    them, also the mean engine clock over each dispatch: its active cycles, summed
+    over the dies, per ns of the dispatch's own timestamps, divided by the die count
+    (meaningful for dispatches much longer than the counter window's few-us
+    overhang, i.e. not for the short merge kernels)."""
     vals = {}
     for r in csv.DictReader(open(pmc_csv)):
         if "copyBuffer" in r["Kernel_Name"]:
             continue
         key = (short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
-        vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        v = float(r["Counter_Value"])
+        vals.setdefault(key, []).append(v)
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            vals.setdefault((key[0], "clock_GHz"), []).append(v / max(dur, 1) / XCDS)
     counters = sorted({c for _, c in vals})
     kernels = sorted({k for k, _ in vals})
     out = ["# rocprofv3 hardware counters, mean per dispatch", "# command:", "#   " + command,

@@ -157,3 +157,24 @@ def test_every_timing_event_is_used_once_before_its_timed_launch(iters, warmup):
     assert len(untimed) >= max(warmup, iters)
     warmed = {(id(a), id(b)) for a, b in untimed if a is not None}
     assert all((id(a), id(b)) in warmed for a, b in timed)
+
+
+def test_counter_summary_clock_column(tmp_path):
+    # GRBM_GUI_ACTIVE summed over the 8 dies: 8 x 2.0e6 cycles over a 1 ms dispatch
+    # is a 2.0 GHz engine clock; the calibration copy is left out.
+    hdr = ("Correlation_Id,Dispatch_Id,Agent_Id,Queue_Id,Process_Id,Thread_Id,Grid_Size,Kernel_Id,"
+           "Kernel_Name,Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,Accum_VGPR_Count,"
+           "SGPR_Count,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp")
+    rows = [
+        '1,1,"Agent 1",1,1,1,512,7,"__amd_rocclr_copyBuffer",512,0,0,8,0,32,"GRBM_GUI_ACTIVE",5.0e6,0,1000',
+        '2,2,"Agent 1",1,1,1,512,8,"mla_combine_kernel",256,0,0,8,0,32,"GRBM_GUI_ACTIVE",1.6e7,0,1000000',
+        '3,3,"Agent 1",1,1,1,512,8,"mla_combine_kernel",256,0,0,8,0,32,"GRBM_GUI_ACTIVE",1.2e7,0,1000000',
+    ]
+    p = tmp_path / "pmc.csv"
+    p.write_text(hdr + "\n" + "\n".join(rows) + "\n")
+    out = bench.summarize_counters(str(p), "cmd").splitlines()
+    head = [l for l in out if l.startswith("kernel")][0].split()
+    line = [l for l in out if l.startswith("mla_combine")][0].split()
+    assert head[-1] == "clock_GHz" and line[1] == "2"
+    assert float(line[head.index("clock_GHz")]) == pytest.approx(1.75)
+    assert float(line[head.index("GRBM_GUI_ACTIVE")]) == pytest.approx(1.4e7)

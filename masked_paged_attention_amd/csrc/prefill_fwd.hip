@@ -540,9 +540,18 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     const long long off = (row * p.kv_head_num + kvh) * D;
     return {(const char*)((const T*)p.k + off), (const char*)((const T*)p.v + off), min(kBN, kv - j0) - 1};
   };
-  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf)
+  // Byte offsets of this lane's rows in the wave's 4 blocks of a full tile
+  // (no clamp), computed once.
+  unsigned off_full[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) off_full[i] = (unsigned)(16 * w + 4 * i + lrow) * kv_row_bytes + lchunk16;
+  // Block 4w + i of a tile whose last key is `last` (kBN - 1: a full tile, the
+  // precomputed offsets; FULL is that fact at compile time).
+  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf, auto FULL)
       __attribute__((always_inline)) {
-    const unsigned off = (unsigned)min(4 * i + lrow, last) * kv_row_bytes + lchunk16;
+    const unsigned off = decltype(FULL)::value ? off_full[i]
+                                               : (unsigned)min(16 * w + 4 * i + lrow, last) * kv_row_bytes + lchunk16;
+    i += 4 * w;
     dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
   };
 
@@ -805,8 +814,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     const TileSrc ts = tile_src(0, block_of(0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      issue_block(0, 4 * w + i, ts.k, ts.last, 0);
-      issue_block(1, 4 * w + i, ts.v, ts.last, 0);
+      issue_block(0, i, ts.k, ts.last, 0, std::false_type{});
+      issue_block(1, i, ts.v, ts.last, 0, std::false_type{});
     }
   }
   __builtin_amdgcn_s_waitcnt(0xF70);
@@ -822,7 +831,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     // Loads of the next iteration's tile (into the other buffer), spread between
     // the QK MFMAs.
     auto issue_next = [&](int k) __attribute__((always_inline)) {
-      if (load_next) issue_block(k & 1, 4 * w + (k >> 1), (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
+      if (load_next) issue_block(k & 1, k >> 1, (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1, std::false_type{});
     };
     if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
       if constexpr (kType == 9 && kTile) {
@@ -838,8 +847,9 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
         s[1] = f32x16{};
       }
       // K operand reads run kQkDepth MFMAs ahead; the next tile's loads sit
-      // between the MFMAs in one straight-line version (no branch between them)
-      // and are left out of the other (last iteration).
+      // between the MFMAs in straight-line versions (no branch between them):
+      // LOAD 2 for a full next tile, 1 for a partial one (rows clamped to its
+      // last key), 0 for none (last iteration).
       auto qk = [&](auto LOAD) __attribute__((always_inline)) {
         auto rd = [&](int i) -> V8 {
           const int c = i >> 1, kb = i & 1;
@@ -854,8 +864,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           const V8 a = ring[i % kQkDepth];
           if (i + kQkDepth < 2 * NC) ring[i % kQkDepth] = rd(i + kQkDepth);
           s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]);
-          if constexpr (decltype(LOAD)::value) {
-            if (i & 1) issue_block((i >> 1) & 1, 4 * w + (i >> 2), ((i >> 1) & 1) ? nx.v : nx.k, nx.last, buf ^ 1);
+          if constexpr (decltype(LOAD)::value > 0) {
+            if (i & 1)
+              issue_block((i >> 1) & 1, i >> 2, ((i >> 1) & 1) ? nx.v : nx.k, nx.last, buf ^ 1,
+                          std::bool_constant<decltype(LOAD)::value == 2>{});
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -864,10 +876,12 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       // waves sharing a SIMD, one in its softmax yields issue slots to one
       // feeding the matrix cores, which spreads the two waves' phases apart.
       __builtin_amdgcn_s_setprio(2);
-      if (load_next) {
-        qk(std::true_type{});
+      if (!load_next) {
+        qk(std::integral_constant<int, 0>{});
+      } else if (!kTile && nx.last == kBN - 1) {  // (the tile variants keep their registers)
+        qk(std::integral_constant<int, 2>{});
       } else {
-        qk(std::false_type{});
+        qk(std::integral_constant<int, 1>{});
       }
       // block id two iterations ahead, read while the softmax runs
       blk_next = block_of(u + 2);

@@ -237,6 +237,7 @@ def summarize_traffic(fetch_csv, write_csv, command, copy_bytes=1 << 30):
 
 
 XCDS = 8  # accelerator complex dies of an MI355X, each with its own GRBM_GUI_ACTIVE
+CUS = 256  # compute units of an MI355X
 
 
 def summarize_counters(pmc_csv, command):
@@ -256,6 +257,14 @@ def summarize_counters(pmc_csv, command):
         if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
             dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             vals.setdefault((key[0], "clock_GHz"), []).append(v / max(dur, 1) / XCDS)
+    # LDS busy share: cycles the LDS served indexed reads and writes, summed over
+    # the compute units, per compute-unit cycle of the dispatch (the definition of
+    # rocprofv3's LdsUtil, with the per-die active cycles taken as their mean)
+    for k in {k for k, c in vals if c == "SQ_LDS_IDX_ACTIVE"}:
+        if (k, "GRBM_GUI_ACTIVE") in vals:
+            lds = float(np.mean(vals[(k, "SQ_LDS_IDX_ACTIVE")]))
+            gui = float(np.mean(vals[(k, "GRBM_GUI_ACTIVE")])) / XCDS
+            vals[(k, "lds_busy_pct")] = [100.0 * lds / max(gui * CUS, 1.0)]
     counters = sorted({c for _, c in vals})
     kernels = sorted({k for k, _ in vals})
     out = ["# rocprofv3 hardware counters, mean per dispatch", "# command:", "#   " + command,

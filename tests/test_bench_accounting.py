@@ -178,3 +178,21 @@ def test_counter_summary_clock_column(tmp_path):
     assert head[-1] == "clock_GHz" and line[1] == "2"
     assert float(line[head.index("clock_GHz")]) == pytest.approx(1.75)
     assert float(line[head.index("GRBM_GUI_ACTIVE")]) == pytest.approx(1.4e7)
+
+
+def test_counter_summary_lds_busy_column(tmp_path):
+    # 8 dies x 1.0e6 active cycles; 256 CUs x 1.0e6 x 25% = 6.4e7 LDS-busy cycles
+    hdr = ("Correlation_Id,Dispatch_Id,Agent_Id,Queue_Id,Process_Id,Thread_Id,Grid_Size,Kernel_Id,"
+           "Kernel_Name,Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,Accum_VGPR_Count,"
+           "SGPR_Count,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp")
+    rows = [
+        '1,1,"Agent 1",1,1,1,512,8,"k",256,0,0,8,0,32,"GRBM_GUI_ACTIVE",8.0e6,0,500000',
+        '1,1,"Agent 1",1,1,1,512,8,"k",256,0,0,8,0,32,"SQ_LDS_IDX_ACTIVE",6.4e7,0,500000',
+    ]
+    p = tmp_path / "pmc.csv"
+    p.write_text(hdr + "\n" + "\n".join(rows) + "\n")
+    out = bench.summarize_counters(str(p), "cmd").splitlines()
+    head = [l for l in out if l.startswith("kernel")][0].split()
+    line = [l for l in out if l.startswith("k ")][0].split()
+    assert float(line[head.index("lds_busy_pct")]) == pytest.approx(25.0)
+    assert float(line[head.index("clock_GHz")]) == pytest.approx(2.0)

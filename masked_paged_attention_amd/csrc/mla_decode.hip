@@ -202,8 +202,8 @@ __global__ void __launch_bounds__(512, 1)
   const long long lat_step = (long long)p.ckv_stride * (long long)sizeof(T);
   const long long rope_step = split_rope ? 64 * (long long)sizeof(T) : lat_step;
   auto issue = [&](const TileRef& tr, T* buf) __attribute__((always_inline)) {
-    const int blk = tr.blk, lj = tr.j;
-    const int last = tr.k1 - 1 - lj;  // last key of the segment within the tile
+    const int blk = tr.blk, tj = tr.j;  // the tile's block id and first key
+    const int last = tr.k1 - 1 - tj;    // last key of the segment within the tile
     const unsigned m0buf = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)buf;
     if constexpr (Q8) {
       // Latent: wave w fills slots 4w .. 4w+3 and the same + 16 (lanes 32..63),
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(512, 1)
       const int ropekey = 8 * w + (ln >> 3);
       const unsigned ropecol = 16u * (unsigned)((ln & 7) ^ rope_swz(ropekey));
       if constexpr (ONE_BLOCK) {
-        const long long rt = (long long)blk * p.block_size + (lj & (p.block_size - 1));
+        const long long rt = (long long)blk * p.block_size + (tj & (p.block_size - 1));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int key = min(lat_slot(4 * w + k) + 16 * half, last);
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(512, 1)
       } else {
         const int32_t* bt = block_tables + (long long)tr.b * p.max_blocks;
         auto row_of = [&](int key) -> long long {
-          const int j = lj + min(key, last);
+          const int j = tj + min(key, last);
           const int bi = j / p.block_size;
           return (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
         };
@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(512, 1)
     }
     if constexpr (ONE_BLOCK) {
       // The tile lies in one cache block: its keys are consecutive rows.
-      const long long rt = (long long)blk * p.block_size + (lj & (p.block_size - 1));
+      const long long rt = (long long)blk * p.block_size + (tj & (p.block_size - 1));
       const char* a = (const char*)lat_row(rt + min(8 * w, last));
       const int advances = last - 8 * w;  // rows after the first that exist
 #pragma unroll
@@ -261,14 +261,14 @@ __global__ void __launch_bounds__(512, 1)
       const int32_t* bt = block_tables + (long long)tr.b * p.max_blocks;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int j = lj + min(8 * w + k, last);
+        const int j = tj + min(8 * w + k, last);
         const int bi = j / p.block_size;
         const long long row = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
         dma16s_m0(lat_row(row), lane16, m0buf + (unsigned)(lat_slot(8 * w + k) * kLatRow * sizeof(T)));
       }
       const int ln = opaque_lane();
       const int key = 8 * w + (ln >> 3);
-      const int j = lj + min(key, last);
+      const int j = tj + min(key, last);
       const int bi = j / p.block_size;
       const long long row = (long long)bt[bi] * p.block_size + (j - bi * p.block_size);
       dma16((const char*)rope_row(row) + 16 * ((ln & 7) ^ rope_swz(key)),

@@ -243,28 +243,37 @@ CUS = 256  # compute units of an MI355X
 def summarize_counters(pmc_csv, command):
     """Per-kernel means over dispatches of every counter in a rocprofv3 --pmc
     counter_collection.csv (device copies left out).  With GRBM_GUI_ACTIVE among
-    them, also the mean engine clock over each dispatch: its active cycles, summed
-    over the dies, per ns of the dispatch's own timestamps, divided by the die count
+    them, also the engine clock of each dispatch: its active cycles, summed over
+    the dies, per ns of the dispatch's own timestamps, divided by the die count
     (meaningful for dispatches much longer than the counter window's few-us
-    overhang, i.e. not for the short merge kernels)."""
+    overhang, i.e. not for the short merge kernels); with SQ_LDS_IDX_ACTIVE too,
+    the LDS busy share of each dispatch: cycles the LDS served indexed reads and
+    writes, summed over the compute units, per compute-unit cycle (rocprofv3's
+    LdsUtil, with the per-die active cycles taken as their mean).  These two are
+    medians over the dispatches, so that the first, cold dispatch of a process
+    does not weigh in."""
     vals = {}
+    per = {}  # (kernel, dispatch) -> {counter: value, "dur": ns}
     for r in csv.DictReader(open(pmc_csv)):
         if "copyBuffer" in r["Kernel_Name"]:
             continue
-        key = (short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+        k = short_kernel_name(r["Kernel_Name"])
         v = float(r["Counter_Value"])
-        vals.setdefault(key, []).append(v)
-        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
-            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-            vals.setdefault((key[0], "clock_GHz"), []).append(v / max(dur, 1) / XCDS)
-    # LDS busy share: cycles the LDS served indexed reads and writes, summed over
-    # the compute units, per compute-unit cycle of the dispatch (the definition of
-    # rocprofv3's LdsUtil, with the per-die active cycles taken as their mean)
-    for k in {k for k, c in vals if c == "SQ_LDS_IDX_ACTIVE"}:
-        if (k, "GRBM_GUI_ACTIVE") in vals:
-            lds = float(np.mean(vals[(k, "SQ_LDS_IDX_ACTIVE")]))
-            gui = float(np.mean(vals[(k, "GRBM_GUI_ACTIVE")])) / XCDS
-            vals[(k, "lds_busy_pct")] = [100.0 * lds / max(gui * CUS, 1.0)]
+        vals.setdefault((k, r["Counter_Name"]), []).append(v)
+        d = per.setdefault((k, r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = v
+        d["dur"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    clock, lds = {}, {}
+    for (k, _), d in per.items():
+        if "GRBM_GUI_ACTIVE" in d:
+            clock.setdefault(k, []).append(d["GRBM_GUI_ACTIVE"] / max(d["dur"], 1) / XCDS)
+            if "SQ_LDS_IDX_ACTIVE" in d:
+                lds.setdefault(k, []).append(
+                    100.0 * d["SQ_LDS_IDX_ACTIVE"] / max(d["GRBM_GUI_ACTIVE"] / XCDS * CUS, 1.0))
+    for k, v in clock.items():
+        vals[(k, "clock_GHz")] = [float(np.median(v))]
+    for k, v in lds.items():
+        vals[(k, "lds_busy_pct")] = [float(np.median(v))]
     counters = sorted({c for _, c in vals})
     kernels = sorted({k for k, _ in vals})
     out = ["# rocprofv3 hardware counters, mean per dispatch", "# command:", "#   " + command,

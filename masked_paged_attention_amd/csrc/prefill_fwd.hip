@@ -549,8 +549,15 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   // precomputed offsets; FULL is that fact at compile time).
   auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf, auto FULL)
       __attribute__((always_inline)) {
-    const unsigned off = decltype(FULL)::value ? off_full[i]
-                                               : (unsigned)min(16 * w + 4 * i + lrow, last) * kv_row_bytes + lchunk16;
+    unsigned off;
+    if constexpr (decltype(FULL)::value) {
+      off = off_full[i];
+    } else {
+      // (the row is rebuilt at each use rather than kept per block: registers)
+      int rr = 16 * w + lrow;
+      asm volatile("" : "+v"(rr));
+      off = (unsigned)min(rr + 4 * i, last) * kv_row_bytes + lchunk16;
+    }
     i += 4 * w;
     dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
   };
@@ -623,11 +630,13 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   // linear types)
   float mshift = 0.0f;
   const int a_bq = a_lane / kMaskTile;
-  const T* mrow_diag = nullptr;
-  const T* mrow_back = nullptr;
+  // (byte offsets from the tile's base: a 32-bit lane offset of the row in the
+  // diagonal block, and the wave-uniform distance to its row behind it)
+  unsigned mrow_off = 0;
+  unsigned mback_off = 0;
   if constexpr (kTile) {
-    mrow_diag = (const T*)p.mask + (long long)(a_lane - a_bq * kMaskTile) * p.mask_stride + 4 * g;
-    mrow_back = kType == 9 ? mrow_diag : mrow_diag + (long long)kMaskTile * p.mask_stride;
+    mrow_off = ((unsigned)(a_lane - a_bq * kMaskTile) * (unsigned)p.mask_stride + 4u * g) * (unsigned)sizeof(T);
+    mback_off = kType == 9 ? 0u : (unsigned)kMaskTile * (unsigned)p.mask_stride * (unsigned)sizeof(T);
   }
   auto needs_tile_mask = [&](int t) { return kTileAlibi || (kTile && t * kBN + kBN > w_full_keys); };
   auto load_tile_mask = [&](int t) __attribute__((always_inline)) {
@@ -641,9 +650,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       mshift = mdk > 0 ? -(float)(kMaskTile * (mdk - 1)) : 0.0f;
       if constexpr (kType == 3) mshift *= slope2;
     }
-    const T* src = (mdk == 0 ? mrow_diag : mrow_back) + (j0 & (kMaskTile - 1));
+    const unsigned off = mrow_off + (mdk == 0 ? 0u : mback_off) + (unsigned)(j0 & (kMaskTile - 1)) * (unsigned)sizeof(T);
+    const char* base = (const char*)p.mask;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(src + 8 * u);
+    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(base + off + 16 * u);
   };
 
   // P of tile t from S^T (in s): running max and sum (see the comment above).
@@ -757,6 +767,11 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
               v = (C < vlim && (!kChunked || C >= llim)) ? v : -INFINITY;
             x[kb][r] = v;
             m = fmaxf(m, v);
+            // (sqrt tile: one group of four entries at a time, which keeps
+            // the converted entries' registers few)
+            if constexpr (kTileAlibi && kType == 4) {
+              if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
         return m;
@@ -807,9 +822,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   // landed too, so no wait for Q is left for it to place inside the loop,
   // where it would also drain the tile loads in flight).
   int blk_next = block_of(1);  // block id of the next iteration's tile
-  if constexpr (kTileAlibi) {
-    if (w_active) load_tile_mask(tile_of(0));
-  }
+  // (the tile entries are read by every wave and iteration, unconditionally:
+  // any lane's row offset lies inside the tile, and a branch around the loads
+  // would keep two copies of the entries live)
+  if constexpr (kTileAlibi) load_tile_mask(tile_of(0));
   {
     const TileSrc ts = tile_src(0, block_of(0));
 #pragma unroll
@@ -889,9 +905,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       softmax(t);
       __builtin_amdgcn_s_setprio(2);
       // the next key tile's ALiBi tile entries (this tile's are consumed)
-      if constexpr (kTileAlibi) {
-        if (u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));
-      }
+      if constexpr (kTileAlibi) load_tile_mask(tile_of(min(u + 1, n_tiles - 1)));
       {
         auto rv = [&](int i) -> V8 {
           const int kc = i / NDT, dt = i % NDT;
@@ -916,9 +930,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
       blk_next = block_of(u + 2);
-      if constexpr (kTileAlibi) {
-        if (w_active && u + 1 < n_tiles) load_tile_mask(tile_of(u + 1));
-      }
+      if constexpr (kTileAlibi) load_tile_mask(tile_of(min(u + 1, n_tiles - 1)));
     }
     // The next tile has landed (each wave waits for its own loads; the barrier
     // publishes them and ends every read of this buffer).

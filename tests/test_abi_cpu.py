@@ -41,6 +41,23 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(SIGNATURES) == names
 
 
+def test_no_kernel_spills_to_scratch(lib):
+    """Every device kernel of the library fits its registers: the compiler's
+    resource report, written by the build, shows no scratch (private memory)
+    for any of them, and no kernel asks for more than 512 registers."""
+    from masked_paged_attention_amd.build import RESOURCES
+    assert os.path.exists(RESOURCES), "build the library first (its build writes the report)"
+    res = json.load(open(RESOURCES))
+    names = " ".join(res)
+    for k in ("prefill_dma_kernel", "prefill_fwd_kernel", "mla_split_kernel", "mla_combine_kernel",
+              "lse_merge_kernel"):
+        assert k in names, k
+    assert len(res) >= 60
+    for name, r in res.items():
+        assert r["scratch"] == 0, f"{name} spills {r['scratch']} bytes per lane"
+        assert r["vgpr"] + r["agpr"] <= 512, name
+
+
 def test_constants_match_pages():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "atb_constants.json")))
     d = _header_defines()

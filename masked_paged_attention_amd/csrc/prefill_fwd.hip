@@ -888,10 +888,11 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      // Wave priority 2 for the matrix phases, 0 for the softmax: of the two
+      // Wave priorities 3 for QK, 1 for PV, 0 for the softmax: of the two
       // waves sharing a SIMD, one in its softmax yields issue slots to one
-      // feeding the matrix cores, which spreads the two waves' phases apart.
-      __builtin_amdgcn_s_setprio(2);
+      // feeding the matrix cores, and one starting a tile's QK goes ahead of
+      // one finishing a PV, which spreads the two waves' phases apart.
+      __builtin_amdgcn_s_setprio(3);
       if (!load_next) {
         qk(std::integral_constant<int, 0>{});
       } else if (!kTile && nx.last == kBN - 1) {  // (the tile variants keep their registers)
@@ -903,7 +904,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       blk_next = block_of(u + 2);
       __builtin_amdgcn_s_setprio(0);
       softmax(t);
-      __builtin_amdgcn_s_setprio(2);
+      __builtin_amdgcn_s_setprio(1);
       // the next key tile's ALiBi tile entries (this tile's are consumed)
       if constexpr (kTileAlibi) load_tile_mask(tile_of(min(u + 1, n_tiles - 1)));
       {

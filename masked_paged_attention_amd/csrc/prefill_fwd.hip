@@ -946,10 +946,14 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   if (!w_active) return;
   const float l_tot = sum_with_other_half(l_run);
   const int i = wrow0 + lq;
-  if (i >= L) return;
   // A row whose tile hides every key gets O = 0 (and LSE = -inf).
   const float inv = kTile && l_tot == 0.0f ? 0.0f : 1.0f / l_tot;
-  T* orow = (T*)p.out + (qs + i) * q_row_stride + (long long)head * D + 4 * g;
+  // The wave's 32 x 128 output block is staged in LDS (the tile buffers are
+  // free after the loop's last barrier, and no direct load is in flight; each
+  // wave uses 8.7 KB of its own), so that every global store writes whole
+  // 256-byte rows: lane l of pass k stores 16 bytes of row 4k + l / 16.
+  constexpr int kOutRow = kRowBytes + 16;  // staged row, padded against bank conflicts
+  char* ostage = lds + w * (kRowsPerWave * kOutRow);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -957,9 +961,23 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       V4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (T)(o[dt][4 * rg + e] * inv);
-      *(V4*)(orow + 32 * dt + 8 * rg) = v;
+      *(V4*)(ostage + lq * kOutRow + (int)sizeof(T) * (32 * dt + 8 * rg + 4 * g)) = v;
     }
   }
+  // (the wave's LDS writes complete before its reads below; the clobber keeps
+  // the compiler from moving them across)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  {
+    const int rr = l >> 4, ch = l & 15;
+    T* obase = (T*)p.out + (qs + wrow0) * q_row_stride + (long long)head * D + 8 * ch;
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave / 4; ++k) {
+      const int r = 4 * k + rr;
+      const V8 v = *(const V8*)(ostage + r * kOutRow + 16 * ch);
+      if (wrow0 + r < L) *(V8*)(obase + (long long)r * q_row_stride) = v;
+    }
+  }
+  if (i >= L) return;
   if (p.lse != nullptr && g == 0) {
     float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     if constexpr (kType == 5) lse += p.slopes[head] * (float)(kTile ? a_bq * kMaskTile : a_lane);

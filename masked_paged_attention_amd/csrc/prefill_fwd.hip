@@ -421,15 +421,21 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
 // (V^T transpose read) -- then hit distinct bank groups, and each lane needs 4
 // base addresses per pattern (the rest are immediate offsets).
 //
-// With an ALiBi mask the key tiles are visited from the last one down: the
-// largest biases sit next to the diagonal, so the running max is set by the
-// first tile and rarely moves, and a tile that every row sees needs no max at
-// all -- P = exp2(score - m_run) is formed at once, and a lane's partial row
-// sum above 2^8 (the only way some P can exceed 2^8) sends the tile through
-// the full path, which finds the tile max and moves the reference.  The result
-// is the same either way: only the reference of the exponent differs.  Other
-// masks visit the tiles in key order (the workgroups of one head then sweep
-// the cache together) and always take the full path.
+// With an ALiBi mask the two key tiles nearest the diagonal come first (the
+// last one, then the one before: between them they hold every wave's diagonal
+// when the workgroup has 128 rows), then the rest in key order from the
+// first.  The largest biases sit next to the diagonal, so the running max is
+// set by the first tiles and rarely moves, and a tile that every row sees
+// needs no max at all -- P = exp2(score - m_run) is formed at once, and a
+// lane's partial row sum above 2^8 (the only way some P can exceed 2^8) sends
+// the tile through the full path, which finds the tile max and moves the
+// reference.  The result is the same either way: only the reference of the
+// exponent differs.  After the diagonal tiles, the workgroups of one head
+// that run side by side read the same key tiles at about the same time, so
+// they share them in L2 (visiting every tile from the diagonal down, they
+// would read each tile two steps apart, a reuse distance that fills the L2 of
+// a die).  Other masks visit the tiles in key order and always take the full
+// path.
 template <typename T, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
                                                              const int32_t* __restrict__ block_tables) {
@@ -527,7 +533,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const int lrow = l >> 4;
   const unsigned lchunk16 = 16u * (unsigned)((l & 15) ^ (4 * lrow));
   const unsigned lds_base = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds;
-  auto tile_of = [&](int u) { return kReverse ? n_tiles - 1 - u : t_lo + u; };
+  auto tile_of = [&](int u) { return kReverse ? (u < 2 ? n_tiles - 1 - u : u - 2) : t_lo + u; };
   auto block_of = [&](int u) -> int { return (u < n_tiles) ? btab[(tile_of(u) * kBN) >> p.bs_shift] : 0; };
   struct TileSrc {
     const char* k;

@@ -305,14 +305,23 @@ def read_traffic(kernel_prefix, path=TRAFFIC_SUMMARY):
 # ---------------------------------------------------------------------------
 
 
+PREWARM_S = 0.5  # untimed steps before the warm-up steps (clock ramp)
+EXTRA_PREWARM_S = 0.25  # the same before each of the other workloads
+
+
 def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_op(torch, run, iters, warmup):
+def time_op(torch, run, iters, warmup, prewarm_s=EXTRA_PREWARM_S):
     """Average ms of run() over iters launches, events on the current stream (for
-    calls without an operation object)."""
-    for _ in range(warmup):
+    calls without an operation object); about prewarm_s seconds of untimed calls
+    first (clock ramp, as in time_ops)."""
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    n = max(warmup, int(prewarm_s / max(time.perf_counter() - t0, 1e-4)))
+    for _ in range(n):
         run()
     torch.cuda.synchronize()
     evs = [_events(torch) for _ in range(iters)]
@@ -334,14 +343,28 @@ def launch_events(torch, n):
     return evs
 
 
-def time_ops(torch, ops, iters, warmup):
+def time_ops(torch, ops, iters, warmup, prewarm_s=EXTRA_PREWARM_S):
     """Average ms of one call over iters back-to-back calls of the operations in turn,
     from events recorded on each call's own kernels (its first kernel's start, its
     last kernel's end: mpaOperationSetLaunchEvents), so no command sits between the
     calls on the stream.  The warm-up calls carry the same events: the first
     launch that records a given event that way runs several times slower, and
-    must not be a timed one."""
+    must not be a timed one.  Before them, about prewarm_s seconds of untimed
+    calls run back to back, so that the clocks have left their idle state (the
+    inputs of each workload are made on the host first, and the GPU idles
+    meanwhile)."""
     evs = launch_events(torch, iters)
+    if prewarm_s > 0:
+        t0 = time.perf_counter()
+        ops[0].set_launch_events(*evs[0])
+        ops[0].run()
+        torch.cuda.synchronize()
+        n = max(1, int(prewarm_s / max(time.perf_counter() - t0, 1e-4)))
+        for i in range(n):
+            op = ops[i % len(ops)]
+            op.set_launch_events(*evs[i % iters])
+            op.run()
+        torch.cuda.synchronize()
     for i in range(max(warmup, iters)):
         op = ops[i % len(ops)]
         op.set_launch_events(*evs[i % iters])
@@ -461,7 +484,7 @@ def _sum_or_none(*xs):
 
 # The step's prefill workload (the sqrt call; the left-aligned call reads the same inputs).
 HEADLINE = "alibi_sqrt_16384"
-PREWARM_S = 0.5  # untimed steps before the warm-up steps (clock ramp)
+
 
 
 def main():

@@ -412,9 +412,9 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
   }
 }
 
-// headSize 128 with a power-of-two blockSize >= 64 (every 64-key tile inside one
-// cache block): the same computation, with K and V tiles brought into LDS by
-// direct global->LDS loads (no register staging).  LDS layout of a tile: 16
+// headSize 128 with a power-of-two blockSize >= 16 (each wave's 16 rows of a
+// 64-key tile inside one cache block): the same computation, with K and V
+// tiles brought into LDS by direct global->LDS loads (no register staging).  LDS layout of a tile: 16
 // blocks of 4 rows (1 KB, one load instruction each) plus 16 bytes of padding;
 // inside a block the 16-byte chunks of row m are XOR-swizzled by 4m.  Both read
 // patterns -- 32 rows at one 16-byte column (QK operand) and 4 rows x 64 bytes
@@ -534,38 +534,52 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   const unsigned lchunk16 = 16u * (unsigned)((l & 15) ^ (4 * lrow));
   const unsigned lds_base = (unsigned)(unsigned long)(const __attribute__((address_space(3))) void*)lds;
   auto tile_of = [&](int u) { return kReverse ? (u < 2 ? n_tiles - 1 - u : u - 2) : t_lo + u; };
-  auto block_of = [&](int u) -> int { return (u < n_tiles) ? btab[(tile_of(u) * kBN) >> p.bs_shift] : 0; };
+  // The wave's 16 rows of a tile lie in one cache block (blockSize >= 16, a
+  // power of two, and tiles start at multiples of 64): its loads take one
+  // wave-uniform base, at the first row of its 16-row group -- clamped to the
+  // group of the tile's last key when the wave's rows are all past it, so that
+  // no block-table entry past the sequence's keys is read.
+  auto wave_row0 = [&](int last) { return min(16 * w, last & ~15); };
+  auto tile_last = [&](int u) { return min(kBN, kv - tile_of(u) * kBN) - 1; };
+  auto block_of = [&](int u) -> int {
+    return (u < n_tiles) ? btab[(tile_of(u) * kBN + wave_row0(tile_last(u))) >> p.bs_shift] : 0;
+  };
   struct TileSrc {
-    const char* k;
+    const char* k;  // the wave's first row (wave_row0) of the tile, K and V
     const char* v;
-    int last;
+    int last;       // the tile's last key, counted from that row
+    int d0;         // the wave's own first row, counted from that row
+    bool full;      // a tile of kBN keys
   };
   auto tile_src = [&](int u, int blk) -> TileSrc {
     const int j0 = tile_of(u) * kBN;
-    const long long row = (long long)blk * p.block_size + (j0 & (p.block_size - 1));
+    const int last = min(kBN, kv - j0) - 1;
+    const int r0 = wave_row0(last);
+    const long long row = (long long)blk * p.block_size + ((j0 + r0) & (p.block_size - 1));
     const long long off = (row * p.kv_head_num + kvh) * D;
-    return {(const char*)((const T*)p.k + off), (const char*)((const T*)p.v + off), min(kBN, kv - j0) - 1};
+    return {(const char*)((const T*)p.k + off), (const char*)((const T*)p.v + off), last - r0, 16 * w - r0,
+            last == kBN - 1};
   };
   // Byte offsets of this lane's rows in the wave's 4 blocks of a full tile
   // (no clamp), computed once.
   unsigned off_full[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) off_full[i] = (unsigned)(16 * w + 4 * i + lrow) * kv_row_bytes + lchunk16;
-  // Block 4w + i of a tile whose last key is `last` (kBN - 1: a full tile, the
-  // precomputed offsets; FULL is that fact at compile time).
-  auto issue_block = [&](int kind, int i, const char* tile_base, int last, int buf, auto FULL)
-      __attribute__((always_inline)) {
+  for (int i = 0; i < 4; ++i) off_full[i] = (unsigned)(4 * i + lrow) * kv_row_bytes + lchunk16;
+  // Block 4w + i of tile `ts` (FULL: a tile of kBN keys, known at compile time:
+  // the precomputed offsets; else rows clamped to the last key).
+  auto issue_block = [&](int kind, int i, const TileSrc& ts, int buf, auto FULL) __attribute__((always_inline)) {
     unsigned off;
     if constexpr (decltype(FULL)::value) {
       off = off_full[i];
     } else {
       // (the row is rebuilt at each use rather than kept per block: registers)
-      int rr = 16 * w + lrow;
+      int rr = ts.d0 + lrow;
       asm volatile("" : "+v"(rr));
-      off = (unsigned)min(rr + 4 * i, last) * kv_row_bytes + lchunk16;
+      off = (unsigned)min(rr + 4 * i, ts.last) * kv_row_bytes + lchunk16;
     }
     i += 4 * w;
-    dma16s_m0_nomem(tile_base, off, lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
+    dma16s_m0_nomem(kind ? ts.v : ts.k, off,
+                    lds_base + (unsigned)(buf * kBufBytes + kind * kTileBytes + i * kBlkBytes));
   };
 
   // ---- LDS read addresses (bytes, without the buffer offset) ----
@@ -836,8 +850,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     const TileSrc ts = tile_src(0, block_of(0));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      issue_block(0, i, ts.k, ts.last, 0, std::false_type{});
-      issue_block(1, i, ts.v, ts.last, 0, std::false_type{});
+      issue_block(0, i, ts, 0, std::false_type{});
+      issue_block(1, i, ts, 0, std::false_type{});
     }
   }
   __builtin_amdgcn_s_waitcnt(0xF70);
@@ -853,7 +867,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     // Loads of the next iteration's tile (into the other buffer), spread between
     // the QK MFMAs.
     auto issue_next = [&](int k) __attribute__((always_inline)) {
-      if (load_next) issue_block(k & 1, k >> 1, (k & 1) ? nx.v : nx.k, nx.last, buf ^ 1, std::false_type{});
+      if (load_next) issue_block(k & 1, k >> 1, nx, buf ^ 1, std::false_type{});
     };
     if (t < w_tiles && (!kChunked || t >= w_t_lo)) {
       if constexpr (kType == 9 && kTile) {
@@ -888,8 +902,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
           s[i & 1] = mfma32(a, qreg[i >> 1], s[i & 1]);
           if constexpr (decltype(LOAD)::value > 0) {
             if (i & 1)
-              issue_block((i >> 1) & 1, i >> 2, ((i >> 1) & 1) ? nx.v : nx.k, nx.last, buf ^ 1,
-                          std::bool_constant<decltype(LOAD)::value == 2>{});
+              issue_block((i >> 1) & 1, i >> 2, nx, buf ^ 1, std::bool_constant<decltype(LOAD)::value == 2>{});
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -901,7 +914,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       __builtin_amdgcn_s_setprio(3);
       if (!load_next) {
         qk(std::integral_constant<int, 0>{});
-      } else if (!kTile && nx.last == kBN - 1) {  // (the tile variants keep their registers)
+      } else if (!kTile && nx.full) {  // (the tile variants keep their registers)
         qk(std::integral_constant<int, 2>{});
       } else {
         qk(std::integral_constant<int, 1>{});
@@ -994,7 +1007,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s, const LaunchEvents& ev) {
   const dim3 g(grid), blk(256);
-  if (D == 128 && p.bs_shift >= 6) {
+  if (D == 128 && p.bs_shift >= 4) {
     switch (mask_type) {
       case kMaskTileFlag | 3:
         hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 3>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);

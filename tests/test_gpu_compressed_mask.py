@@ -30,6 +30,10 @@ CASES = [
     # headSize 128 with 64- and 256-key cache blocks (the direct-load kernel)
     ([257, 64, 3], [513, 64, 200], 8, 2, 128, 64),
     ([130, 500], [700, 500], 4, 4, 128, 256),
+    # headSize 128 with 16- and 32-key cache blocks (the direct-load kernel, one
+    # block id per wave's 16 rows of a tile)
+    ([200, 77, 9], [457, 333, 9], 8, 2, 128, 16),
+    ([130, 64], [301, 64], 4, 4, 128, 32),
     # headSize 64 with 64- and 256-key cache blocks (one block id per 64-key tile)
     ([190, 70], [450, 70], 4, 2, 64, 64),
     ([300, 5], [520, 300], 4, 4, 64, 256),

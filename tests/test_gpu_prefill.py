@@ -43,6 +43,30 @@ def test_small_all_masks(dtype, D, mask):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("mask", [0, 3, 4, 5, 9])
+def test_head_size_128_small_blocks(dtype, bs, mask):
+    # headSize 128 with 16- and 32-key cache blocks (the direct-load kernel, one
+    # block id per wave's 16 rows of a tile): kvSeqLen 150, 157, 201, 224, 256,
+    # 180, 110 put the last key of the final tile in every 16-row group and on a
+    # tile boundary, with prefixes, GQA and NaN in every slot not to be read
+    log(f"case D=128 bs={bs} dtype={dtype} mask={mask}")
+    c = _case(400 + bs + mask, [150, 67, 1, 211, 256, 100, 110], [0, 90, 200, 13, 0, 80, 0], 4, 2, 128, bs,
+              dtype, mask)
+    out, lse = gpu_prefill(c)
+    check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_head_size_128_small_blocks_gqa4(bs):
+    log(f"case D=128 bs={bs} GQA 8/2 and MQA 4/1")
+    for H, KVH in ((8, 2), (4, 1)):
+        c = _case(420 + bs + H, [300, 129, 45], [700, 0, 19], H, KVH, 128, bs, "bf16", 4)
+        out, lse = gpu_prefill(c)
+        check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("bs", [64, 128, 256])
 @pytest.mark.parametrize("mask", [0, 3, 4, 5, 9])
 def test_head_size_64_whole_tile_blocks(dtype, bs, mask):
@@ -204,7 +228,7 @@ def test_alibi_score_spikes_move_the_running_max(dtype, mask):
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("D,bs,chunk", [(128, 128, 64), (128, 128, 100), (128, 64, 256), (128, 24, 37),
-                                        (64, 16, 48)])
+                                        (128, 16, 48), (128, 32, 100), (64, 16, 48)])
 def test_chunked_local_mask(dtype, D, bs, chunk):
     # chunked local causal mask: row at absolute a sees keys j <= a of its own chunk
     log(f"case chunked dtype={dtype} D={D} bs={bs} chunk={chunk}")

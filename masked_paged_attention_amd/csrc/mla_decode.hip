@@ -161,11 +161,17 @@ __global__ void __launch_bounds__(512, 1)
     const int4 sg = sload_int4(&segs[ls]);
     lb = sg.x; lj = sg.y; lk1 = sg.z;
   }
-  // With a power-of-two block size >= 32 every tile lies inside one cache block
-  // (tiles start at multiples of 32): one wave-uniform block id per tile.
-  // Otherwise each row looks its block up.
+  // ONE_BLOCK: a power-of-two block size >= 8 (>= 32 with the int8 cache): the 8
+  // keys that a loader wave fetches of a tile (tiles start at multiples of 32)
+  // lie in one cache block -- with the int8 cache the whole tile does -- so
+  // each loader wave takes one wave-uniform block id per tile, that of its
+  // first key (clamped into the group of the segment's last key on a tile
+  // past it, so that no block-table entry past the keys is read).  Otherwise
+  // each row looks its block up.
+  auto wave_key0 = [&](int last) { return Q8 ? 0 : min(8 * w, last & ~7); };
   auto tile_block = [&]() -> int {
-    return ONE_BLOCK ? block_tables[(long long)lb * p.max_blocks + (lj >> p.bs_shift)] : 0;
+    return ONE_BLOCK ? block_tables[(long long)lb * p.max_blocks + ((lj + wave_key0(lk1 - 1 - lj)) >> p.bs_shift)]
+                     : 0;
   };
 
   auto ld_advance = [&]() {
@@ -242,9 +248,10 @@ __global__ void __launch_bounds__(512, 1)
       return;
     }
     if constexpr (ONE_BLOCK) {
-      // The tile lies in one cache block: its keys are consecutive rows.
-      const long long rt = (long long)blk * p.block_size + (tj & (p.block_size - 1));
-      const char* a = (const char*)lat_row(rt + min(8 * w, last));
+      // The wave's keys lie in one cache block, from its key k0 on: consecutive rows.
+      const int k0 = wave_key0(last);
+      const long long rt = (long long)blk * p.block_size + ((tj + k0) & (p.block_size - 1));
+      const char* a = (const char*)lat_row(rt + min(8 * w, last) - k0);
       const int advances = last - 8 * w;  // rows after the first that exist
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -254,7 +261,7 @@ __global__ void __launch_bounds__(512, 1)
       // Rope: lane l carries key 8w + l/8 (clamped), 16-byte chunk (l % 8) ^ rope_swz(key).
       const int ln = opaque_lane();
       const int key = 8 * w + (ln >> 3);
-      const unsigned off = (unsigned)min(key, last) * (unsigned)rope_step +
+      const unsigned off = (unsigned)(min(key, last) - k0) * (unsigned)rope_step +
                            16u * (unsigned)((ln & 7) ^ rope_swz(key));
       dma16s(rope_row(rt), off, buf + kLatElems + 64 * 8 * w);
     } else {
@@ -757,7 +764,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaParams p, const int
 
 template <typename T, bool Q8>
 void launch_split(const MlaParams& p, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  if (p.bs_shift >= 5)
+  if (p.bs_shift >= (Q8 ? 5 : 3))
     hipExtLaunchKernelGGL((mla_split_kernel<T, true, Q8>), dim3(p.grid), dim3(512), 0, s, start, stop, 0, p,
                           p.block_tables, p.segs, p.piece_seg, p.seqs, p.seqs2);
   else

@@ -32,6 +32,24 @@ def test_spec_decode_128_heads(mask):
     check_mla(c, out, lse)
 
 
+@pytest.mark.parametrize("bs", [8, 16])
+@pytest.mark.parametrize("cache_mode", [0, 1])
+def test_small_block_sizes(bs, cache_mode):
+    # 8- and 16-key cache blocks: one block id per loader wave's 8 keys of a tile;
+    # contexts ending in every 8-key group of a 32-key tile, q_len 1..4 with the
+    # SPEC mask, sequences cut across pieces (128 heads), NaN in unread slots
+    log(f"case mla blockSize {bs} cacheMode {cache_mode}")
+    ctx = [100, 37, 300, 1, 9, 17, 26, 2049, 771]
+    ql = [1, 2, 4, 1, 3, 1, 2, 4, 1]
+    c = W.make_mla(75 + bs, ctx, ql, 128, bs, "bf16", 1, 1, cache_mode, 1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    rng = np.random.default_rng(9)
+    T = c.n_tokens
+    rows = sorted({(int(rng.integers(T)), int(rng.integers(128))) for _ in range(300)} |
+                  {(t, h) for t in range(T) for h in (0, 127)})
+    check_mla(c, out, lse, rows=rows)
+
+
 def test_odd_block_size_and_heads():
     log("case mla blockSize 24, 20 heads, q_len 3")
     c = W.make_mla(65, [95, 48, 3], [3, 3, 3], 20, 24, "bf16", 1, 1, 0, 0.05, poison=True).to(DEV)

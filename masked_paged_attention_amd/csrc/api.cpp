@@ -492,6 +492,7 @@ mpaStatus make_mla_op(const void* qNope, const void* qRope, const void* ctKV, co
   p.batch = batch;
   p.max_rows = plan.max_rows;
   p.any_parts = any_parts ? 1 : 0;
+  p.whole = plan.whole ? 1 : 0;
   p.scale2 = qkScale * kLog2e;
   p.quant = quant ? 1 : 0;
   p.qk_descale = qkDescale;

@@ -72,6 +72,7 @@ struct MlaParams {
   int batch;
   int max_rows;                // largest q_len * H (combine grid)
   int any_parts;               // some sequence has partial results to merge
+  int whole;                   // whole-sequence plan: workgroup i = piece i / row_groups, row group i % row_groups
   float scale2;                // qkScale * log2(e)
   int quant;                   // 1: int8 qNope / ctKV with per-head descales
   const float* qk_descale;     // [H] (quant only)

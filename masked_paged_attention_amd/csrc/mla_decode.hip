@@ -126,9 +126,11 @@ __global__ void __launch_bounds__(512, 1)
   // Workgroup -> (piece, row group): workgroups go round-robin to the 8 XCDs by
   // id; XCD x handles pieces [x * ppx, (x + 1) * ppx), the row groups of one
   // piece side by side.
+  // (whole-sequence plans: workgroup i handles piece i / row_groups, so the row
+  // groups of a sequence go round-robin to the XCDs)
   const int slot = blockIdx.x >> 3;
-  const int piece = (blockIdx.x & 7) * p.pieces_per_xcd + slot / p.row_groups;
-  const int rg = slot % p.row_groups;
+  const int piece = p.whole ? (int)blockIdx.x / p.row_groups : (blockIdx.x & 7) * p.pieces_per_xcd + slot / p.row_groups;
+  const int rg = p.whole ? (int)blockIdx.x % p.row_groups : slot % p.row_groups;
   const int s_beg = piece_seg[piece];
   const int s_end = piece_seg[piece + 1];
   const int row_base = rg * kRows;  // first row (token-major (token, head) index) of this workgroup
@@ -138,10 +140,22 @@ __global__ void __launch_bounds__(512, 1)
     while (s < s_end && sload_int4(&seqs2[sload_int4(&segs[s]).x]).y <= row_base) ++s;
     return s;
   };
+  // End (exclusive) of the keys of segment sg that this row group visits: with
+  // the SPEC mask a whole-sequence segment stops at its last row's limit,
+  // ctx - q_len + t + 1 for the group's last token t (keys after it are hidden
+  // from every row of the group); a partial segment keeps its end, since its
+  // result is merged with the sequence's other segments.
+  auto seg_keys_end = [&](const int4& sg) -> int {
+    if (!p.spec_mask || sg.w >= 0) return sg.z;
+    const int4 sq = sload_int4(&seqs[sg.x]);
+    const int4 sq2 = sload_int4(&seqs2[sg.x]);
+    const int t_last = min(sq2.y - 1, row_base + kRows - 1) / p.head_num;
+    return min(sg.z, sq.x - sq.y + t_last + 1);
+  };
   int n_total = 0;
   for (int s = next_valid(s_beg); s < s_end; s = next_valid(s + 1)) {
     const int4 sg = sload_int4(&segs[s]);
-    n_total += (sg.z - sg.y + kBN - 1) / kBN;
+    n_total += (seg_keys_end(sg) - sg.y + kBN - 1) / kBN;
   }
   if (n_total == 0) return;
 
@@ -159,7 +173,7 @@ __global__ void __launch_bounds__(512, 1)
   int lb, lj, lk1;
   {
     const int4 sg = sload_int4(&segs[ls]);
-    lb = sg.x; lj = sg.y; lk1 = sg.z;
+    lb = sg.x; lj = sg.y; lk1 = seg_keys_end(sg);
   }
   // ONE_BLOCK: a power-of-two block size >= 8 (>= 32 with the int8 cache): the 8
   // keys that a loader wave fetches of a tile (tiles start at multiples of 32)
@@ -180,7 +194,7 @@ __global__ void __launch_bounds__(512, 1)
       ls = next_valid(ls + 1);
       if (ls < s_end) {
         const int4 sg = sload_int4(&segs[ls]);
-        lb = sg.x; lj = sg.y; lk1 = sg.z;
+        lb = sg.x; lj = sg.y; lk1 = seg_keys_end(sg);
       }
     }
   };
@@ -630,7 +644,7 @@ __global__ void __launch_bounds__(512, 1)
     cs = next_valid(cs + 1);
     if (cs < s_end) {
       const int4 sg = sload_int4(&segs[cs]);
-      cj = sg.y; ck1 = sg.z;
+      cj = sg.y; ck1 = seg_keys_end(sg);
     }
     return true;
   };

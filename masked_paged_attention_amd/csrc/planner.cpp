@@ -134,6 +134,63 @@ MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_n
     plan.max_rows = std::max(plan.max_rows, q_len[b] * head_num);
   }
   plan.row_groups = (int)ceil_div(plan.max_rows, kMlaRowsPerGroup);
+
+  plan.seqs.resize(batch);
+  {
+    int64_t tok = 0;
+    for (int b = 0; b < batch; ++b) {
+      MlaSeq& s = plan.seqs[b];
+      s.ctx = ctx[b];
+      s.q_len = q_len[b];
+      s.tok0 = (int32_t)tok;
+      s.rows = q_len[b] * head_num;
+      tok += q_len[b];
+    }
+    plan.tokens = tok;
+  }
+
+  // Whole sequences, when a longest-first schedule of the (sequence, row group)
+  // pairs (key tiles + 1.5 per workgroup) ends within 10% of a perfect balance.
+  {
+    std::vector<int> order(batch);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return ctx[x] > ctx[y]; });
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int i = 0; i < std::max(1, slots); ++i) free_at.push(0.0);
+    double end = 0.0, sum = 0.0;
+    for (int b : order) {
+      const double w = (double)ceil_div(ctx[b], kMlaKeyTile) + 1.5;
+      for (int64_t r = 0; r < ceil_div(plan.seqs[b].rows, kMlaRowsPerGroup); ++r) {
+        const double t = free_at.top() + w;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+        sum += w;
+      }
+    }
+    if (end <= 1.1 * sum / std::max(1, slots) && (int64_t)batch * plan.row_groups < ((int64_t)1 << 30)) {
+      plan.whole = true;
+      plan.pieces_per_xcd = 1;
+      for (int b : order) {
+        plan.piece_seg.push_back((int32_t)plan.segs.size());
+        MlaSegment sg;
+        sg.b = b;
+        sg.k0 = 0;
+        sg.k1 = ctx[b];
+        sg.part = -1;
+        plan.segs.push_back(sg);
+      }
+      plan.piece_seg.push_back((int32_t)plan.segs.size());
+      plan.grid = (int)(batch * (int64_t)plan.row_groups);
+      for (MlaSeq& s : plan.seqs) {
+        s.n_parts = 0;
+        s.part_row0 = 0;
+      }
+      plan.part_rows = 0;
+      return plan;
+    }
+  }
+
   plan.pieces_per_xcd = std::max(1, slots / (kNumXcd * plan.row_groups));
   const int64_t total = tile0[batch];
   // Small problems: no piece shorter than kMinTiles tiles (the rest stay empty).
@@ -141,18 +198,6 @@ MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_n
   const int64_t n_pieces = (int64_t)kNumXcd * plan.pieces_per_xcd;
   const int64_t used = std::max<int64_t>(1, std::min<int64_t>(n_pieces, ceil_div(total, kMinTiles)));
   plan.grid = (int)(n_pieces * plan.row_groups);
-
-  plan.seqs.resize(batch);
-  int64_t tok = 0;
-  for (int b = 0; b < batch; ++b) {
-    MlaSeq& s = plan.seqs[b];
-    s.ctx = ctx[b];
-    s.q_len = q_len[b];
-    s.tok0 = (int32_t)tok;
-    s.rows = q_len[b] * head_num;
-    tok += q_len[b];
-  }
-  plan.tokens = tok;
 
   // Piece p covers flattened tiles [p * total / used, (p + 1) * total / used).
   std::vector<int32_t> n_seg(batch, 0);

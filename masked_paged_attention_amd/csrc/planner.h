@@ -76,10 +76,18 @@ struct MlaPlan {
   int64_t part_rows = 0;       // partial-result rows in the workspace
   int64_t tokens = 0;
   int max_rows = 0;            // largest q_len * head_num
+  // Whole sequences: every piece is one sequence (one segment, no partial
+  // results); workgroup i handles piece i / row_groups, row group i % row_groups,
+  // so a sequence's row groups spread over all XCDs.
+  bool whole = false;
 };
 
 // Plans the split-KV MLA launch for `slots` workgroups resident at once (one per
-// compute unit).  The key tiles of all sequences are laid end to end and cut
+// compute unit).  When the (sequence, row group) pairs are many -- a prefill of
+// long prompts at 128 heads -- and a longest-first schedule of them on the slots
+// ends within 10% of a perfect balance, the plan takes whole sequences instead
+// (MlaPlan::whole: no key split, no partial results, sequences longest first).
+// Otherwise:  The key tiles of all sequences are laid end to end and cut
 // into 8 * pieces_per_xcd pieces of near-equal tile counts; every piece is
 // processed by row_groups workgroups (one per 128-row group) that sit on one XCD,
 // and consecutive pieces go to the same XCD, so the segments of one sequence

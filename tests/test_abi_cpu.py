@@ -315,6 +315,20 @@ def test_mla_plan_pieces_are_balanced(spec):
     assert max(tiles.values()) - min(tiles.values()) <= 1
 
 
+def test_mla_plan_whole_sequences_for_long_prompts():
+    """A prefill of long prompts at 128 heads has many (sequence, row group) pairs
+    whose longest-first schedule balances: one segment per sequence, longest
+    first, no key split.  The decode shapes keep the split (checked above)."""
+    import masked_paged_attention_amd as mpa
+    ctx = np.array([1024, 4096, 2048, 3072])
+    segs = mpa.plan_mla(ctx, np.full(4, 256), 128, 3)
+    assert [tuple(int(v) for v in x) for x in segs] == [(1, 0, 4096, 0, 0), (3, 0, 3072, 0, 1),
+                                                       (2, 0, 2048, 0, 2), (0, 0, 1024, 0, 3)]
+    # a few sequences whose row groups cannot balance stay split
+    segs = mpa.plan_mla(np.array([9000, 300]), np.array([2, 256]), 128, 3)
+    assert len(segs) > 2
+
+
 def test_mla_plan_small_problem_uses_few_pieces():
     import masked_paged_attention_amd as mpa
     segs = mpa.plan_mla(np.array([65, 130, 9]), None, 16, 0)

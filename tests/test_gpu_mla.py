@@ -132,6 +132,34 @@ def test_prefill_128_heads_sampled():
     check_mla(c, out, lse, rows=rows)
 
 
+def _prefill_rows(c, n, seed):
+    rng = np.random.default_rng(seed)
+    T, H = c.n_tokens, c.head_num
+    tok0 = np.concatenate([[0], np.cumsum(c.q_seq_len)[:-1]])
+    edge = {(int(t0) + t, h) for t0, q in zip(tok0, c.q_seq_len) for t in (0, 1, int(q) - 1) for h in (0, 63, 127)}
+    return sorted({(int(rng.integers(T)), int(rng.integers(H))) for _ in range(n)} | edge)
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_prefill_whole_sequences(mask):
+    # long prompts at 128 heads: the whole-sequence plan (no key split, no merge),
+    # each row group's key range ending at its last token's limit under the mask
+    log(f"case mla prefill whole sequences q_len 200..256 H 128 mask={mask}")
+    c = W.make_mla(77 + mask, [1024, 2048, 700, 1500], [256, 256, 200, 256], 128, 128, "bf16", mask, 3, 1,
+                   1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse, rows=_prefill_rows(c, 300, 12 + mask))
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_int8_prefill_whole_sequences():
+    log("case mla int8 prefill whole sequences q_len 256 H 128 causal")
+    c = W.make_mla_int8(79, [1024, 2048, 700, 1500], [256, 256, 200, 256], 128, 128, "bf16", 1, 3,
+                        1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse, rows=_prefill_rows(c, 200, 14))
+
+
 # ---- int8 latent cache (qNope / ctKV int8, per-head qkDescale / pvDescale) ----
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

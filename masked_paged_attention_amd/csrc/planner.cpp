@@ -158,8 +158,10 @@ MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_n
     std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
     for (int i = 0; i < std::max(1, slots); ++i) free_at.push(0.0);
     double end = 0.0, sum = 0.0;
+    int64_t pairs = 0;
     for (int b : order) {
       const double w = (double)ceil_div(ctx[b], kMlaKeyTile) + 1.5;
+      pairs += ceil_div(plan.seqs[b].rows, kMlaRowsPerGroup);
       for (int64_t r = 0; r < ceil_div(plan.seqs[b].rows, kMlaRowsPerGroup); ++r) {
         const double t = free_at.top() + w;
         free_at.pop();
@@ -168,7 +170,10 @@ MlaPlan plan_mla(const int32_t* ctx, const int32_t* q_len, int batch, int head_n
         sum += w;
       }
     }
-    if (end <= 1.1 * sum / std::max(1, slots) && (int64_t)batch * plan.row_groups < ((int64_t)1 << 30)) {
+    // (the grid holds batch x row_groups workgroups, those past a sequence's
+    // rows exiting at once: at most three in four of them may be such)
+    const int64_t grid = (int64_t)batch * plan.row_groups;
+    if (end <= 1.1 * sum / std::max(1, slots) && grid <= 4 * pairs && grid < ((int64_t)1 << 30)) {
       plan.whole = true;
       plan.pieces_per_xcd = 1;
       for (int b : order) {

@@ -152,12 +152,28 @@ def test_prefill_whole_sequences(mask):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("bs", [16, 128])
+def test_prefill_whole_sequences_fp16_concatenated_cache(bs):
+    # the whole-sequence plan over the 576-wide cache (cacheMode 0) in fp16, with
+    # 16-key blocks (one block id per loader wave's 8 keys) and 128-key blocks
+    log(f"case mla prefill whole sequences fp16 cacheMode 0 blockSize {bs}")
+    c = W.make_mla(85 + bs, [900, 1333, 2050, 420], [256, 256, 256, 256], 128, bs, "fp16", 1, 3, 0,
+                   1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse, rows=_prefill_rows(c, 200, 16 + bs))
+
+
 def test_int8_prefill_whole_sequences():
     log("case mla int8 prefill whole sequences q_len 256 H 128 causal")
     c = W.make_mla_int8(79, [1024, 2048, 700, 1500], [256, 256, 200, 256], 128, 128, "bf16", 1, 3,
                         1 / np.sqrt(192), poison=True).to(DEV)
     out, lse = gpu_mla(c)
     check_mla(c, out, lse, rows=_prefill_rows(c, 200, 14))
+    # 16-key blocks: the int8 cache's per-row block lookups
+    c = W.make_mla_int8(80, [777, 1500, 1030, 96], [256, 256, 256, 96], 128, 16, "fp16", 1, 3,
+                        1 / np.sqrt(192), poison=True).to(DEV)
+    out, lse = gpu_mla(c)
+    check_mla(c, out, lse, rows=_prefill_rows(c, 200, 15))
 
 
 # ---- int8 latent cache (qNope / ctKV int8, per-head qkDescale / pvDescale) ----

@@ -686,6 +686,12 @@ def main():
             c = W.make_prefill_config(name, device=dev)
             prefill_extra(name + "_tile", c, W.compressed_tile(c.mask_type, c.dtype).to(dev))
             del c
+        # the same sqrt call over a cache of 16-key blocks (4 blocks per 64-key tile)
+        print("bench: extra alibi_sqrt_16384_bs16", file=sys.stderr, flush=True)
+        c = W.make_prefill(1003, np.array([16384]), np.array([16384]), 40, 40, 128, 16, "bf16", 4,
+                           1.0 / np.sqrt(128.0), slopes="alibi").to(dev)
+        prefill_extra("alibi_sqrt_16384_bs16", c)
+        del c
         for name in ["alibi_sqrt_varlen16", "alibi_sqrt_padded16", "alibi_left_varlen16", "alibi_left_padded16"]:
             print(f"bench: extra {name}", file=sys.stderr, flush=True)
             c = W.make_prefill_config(name, device=dev)

@@ -32,7 +32,7 @@
 //     max and sum need one cross-half permlane swap per row;
 //   * softmax runs in the log2 domain (scale and slopes pre-multiplied by
 //     log2 e) with fp32 running max / sum, scores formed directly relative to
-//     a reference max that only moves when a row's max grows by more than 2^8
+//     a reference max that only moves when a row's max grows by more than 2^10
 //     (so the output is rarely rescaled); P is rounded to the input type for
 //     the PV MFMA.
 
@@ -52,7 +52,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBN = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
+constexpr float kRescaleSlack = 10.0f;  // log2 units of growth tolerated before rescaling
 constexpr int kSqrtFar = 384;  // sqrt ALiBi: distance from which a tile's bias is expanded
 
 template <typename T, int D, int MASK>
@@ -334,8 +334,8 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
         mx = form_scores(std::false_type{});
       }
       mx = max_with_other_half(mx);  // tile max of the row, relative to m_ref
-      // Move the reference only when a row's max grows by more than 2^8 (or on the
-      // row's first visible key): P stays <= 2^8 and the final normalisation uses
+      // Move the reference only when a row's max grows by more than 2^10 (or on the
+      // row's first visible key): P stays <= 2^10 and the final normalisation uses
       // the same reference, so the result is exact; the rescale of O is rare.
       const bool need = (m_run == -INFINITY) ? (mx > -INFINITY) : (mx > kRescaleSlack);
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
 // first.  The largest biases sit next to the diagonal, so the running max is
 // set by the first tiles and rarely moves, and a tile that every row sees
 // needs no max at all -- P = exp2(score - m_run) is formed at once, and a
-// lane's partial row sum above 2^8 (the only way some P can exceed 2^8) sends
+// lane's partial row sum above 2^10 (the only way some P can exceed 2^10) sends
 // the tile through the full path, which finds the tile max and moves the
 // reference.  The result is the same either way: only the reference of the
 // exponent differs.  After the diagonal tiles, the workgroups of one head
@@ -456,7 +456,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   constexpr int kBlkBytes = 4 * kRowBytes + 16;   // 1040
   constexpr int kTileBytes = 16 * kBlkBytes;      // 64 rows
   constexpr int kBufBytes = 2 * kTileBytes;       // K tile, then V tile
-  constexpr float kSumLimit = 256.0f;             // 2^kRescaleSlack
+  constexpr float kSumLimit = 1024.0f;            // 2^kRescaleSlack
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
 
@@ -761,7 +761,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
     }
     if (!done) {
       // Full path: tile max; the reference moves when a row's max grows by
-      // more than 2^8 (or on the row's first visible key).
+      // more than 2^10 (or on the row's first visible key).
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
       const float nbm = -slope2 * dbf - m_ref;
       // scores and the lane max, with or without the per-element predicate

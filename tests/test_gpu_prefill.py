@@ -210,9 +210,10 @@ def test_linear_alibi_zero_tiny_and_negative_scales(dtype, mask, scale):
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("mask", [3, 4, 5])
 def test_alibi_score_spikes_move_the_running_max(dtype, mask):
-    # Keys far from the diagonal with very large dot products: visiting tiles from
-    # the diagonal down, the running max is set early and these keys then exceed
-    # it by far more than 2^8, which must move the reference (the full path).
+    # Keys far from the diagonal with very large dot products: the diagonal tiles
+    # come first, so the running max is set early and these keys then exceed it
+    # by far more than the rescale slack (2^10), which must move the reference
+    # (the full path).
     log(f"case score spikes dtype={dtype} mask={mask}")
     c = W.make_prefill(71 + mask, np.array([700, 300]), np.array([700, 500]), 4, 4, 128, 128, dtype,
                        mask, 1.0 / np.sqrt(128), slopes="alibi", poison=False, name=f"spike-{dtype}-m{mask}")

@@ -434,10 +434,9 @@ __global__ void __launch_bounds__(256, 2) prefill_fwd_kernel(PrefillParams p) {
 // that run side by side read the same key tiles at about the same time, so
 // they share them in L2 (visiting every tile from the diagonal down, they
 // would read each tile two steps apart, a reuse distance that fills the L2 of
-// a die).  Other masks visit the tiles in key order; the generated causal and
-// no-mask rules take the same fast path after their first tile (whose max
-// sets the reference), the compressed norm tile and the chunked mask the full
-// path.
+// a die).  Other masks visit the tiles in key order and take the same fast
+// path after their first tile (whose max sets the reference) on every tile
+// that all rows see whole.
 template <typename T, int MASK>
 __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
                                                              const int32_t* __restrict__ block_tables) {
@@ -716,11 +715,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       }
     };
     bool done = false;
-    // (ALiBi, and the generated causal / no-mask rules: after the first tile
-    // the running max is set, and later tiles exceed it by far less than the
-    // slack unless a score spikes, which the sum test catches)
-    if ((kReverse || (!kTile && (kType == 9 || kType == 0))) && !partial &&
-        __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
+    // (every mask: after the first tile the running max is set, and later tiles
+    // exceed it by far less than the slack unless a score spikes, which the sum
+    // test catches; a tile every row sees carries no tile entries)
+    if (!partial && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
       const float nbm = -slope2 * dbf - m_run;
       float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       // Sqrt ALiBi on a tile whose every distance is >= kSqrtFar: the bias of

@@ -48,6 +48,7 @@ constexpr int kRows = 128;      // query rows per workgroup (4 wave pairs x 32)
 constexpr int kWaves = 8;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units of growth tolerated before rescaling
+constexpr float kSumLimit = 256.0f;    // 2^kRescaleSlack
 
 // LDS layout of one key tile.  Latent part: key k sits in row slot
 // lat_slot(k), 512 values + 8 of padding = 1040 bytes = 65 16-byte chunks.  An
@@ -515,52 +516,79 @@ __global__ void __launch_bounds__(512, 1)
       PV8 vring[kPvDepth];
 #pragma unroll
       for (int c = 0; c < kPvDepth; ++c) vring[c] = load_v(c);
-      // Row max of the scaled scores; the exponent below is fma(s, kmul, -m):
-      // full tiles keep the raw scores (kmul = scale, max taken on the raw
-      // values, exact since scaling is monotonic), partial tiles store the
-      // scaled, masked scores (kmul = 1).
-      float mx = -INFINITY;
-      float kmul = scale2;
-      if (j0 + kBN > w_lim_lo) {
-        // Partial tile: key j0 + 4g + C is visible to this row iff C < vlim.
-        const int vlim = lim - j0 - 4 * (opaque_lane() >> 5);
+      // Fast path, on a tile every row of the wave sees once the reference max
+      // is set: P against the running max at once, checked by the lane's sum
+      // (a P above 2^slack only comes with a sum above it).  If some lane's
+      // sum is larger, the scores are read back from the exchange slots (they
+      // hold this tile's partial scores until the next tile) and take the path
+      // with the row max.  Both waves of a pair see the same scores and take
+      // the same branch.
+      float psum = 0.0f;
+      bool done = false;
+      if (j0 + kBN <= w_lim_lo && __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int C = 8 * (r >> 2) + (r & 3);
-          const float x = (C < vlim) ? s0[r] * scale2 : -INFINITY;
-          s0[r] = x;
-          mx = fmaxf(mx, x);
+          s0[r] = fast_exp2(__builtin_fmaf(s0[r], scale2, -m_run));
+          psum += s0[r];
         }
-        kmul = 1.0f;
-      } else if (scale2 >= 0.0f) {
+        done = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) == 0;
+        if (!done) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-        mx *= scale2;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, -s0[r]);
-        mx *= -scale2;
+          for (int r = 0; r < 16; r += 4) {
+            const float4 u = my_x[16 * r];
+            const float4 v = other_x[16 * r];
+            s0[r] = u.x + v.x; s0[r + 1] = u.y + v.y; s0[r + 2] = u.z + v.z; s0[r + 3] = u.w + v.w;
+          }
+          psum = 0.0f;
+        }
       }
-      mx = max_with_other_half(mx);
-      // Lazy rescale: keep the reference max unless a row grew by > 2^8.  Both
-      // waves of a pair see the same scores and take the same decisions.
-      const bool grow = mx > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        l_run *= alpha;
-        if constexpr (Q8) l16_run *= alpha;
+      if (!done) {
+        // Row max of the scaled scores; the exponent below is fma(s, kmul, -m):
+        // full tiles keep the raw scores (kmul = scale, max taken on the raw
+        // values, exact since scaling is monotonic), partial tiles store the
+        // scaled, masked scores (kmul = 1).
+        float mx = -INFINITY;
+        float kmul = scale2;
+        if (j0 + kBN > w_lim_lo) {
+          // Partial tile: key j0 + 4g + C is visible to this row iff C < vlim.
+          const int vlim = lim - j0 - 4 * (opaque_lane() >> 5);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      float psum = 0.0f;
+          for (int r = 0; r < 16; ++r) {
+            const int C = 8 * (r >> 2) + (r & 3);
+            const float x = (C < vlim) ? s0[r] * scale2 : -INFINITY;
+            s0[r] = x;
+            mx = fmaxf(mx, x);
+          }
+          kmul = 1.0f;
+        } else if (scale2 >= 0.0f) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = fast_exp2(__builtin_fmaf(s0[r], kmul, -m_use));
-        psum += s0[r];
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+          mx *= scale2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, -s0[r]);
+          mx *= -scale2;
+        }
+        mx = max_with_other_half(mx);
+        // Lazy rescale: keep the reference max unless a row grew by > 2^8.  Both
+        // waves of a pair see the same scores and take the same decisions.
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = fmaxf(m_run, mx);
+          const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+          const float alpha = fast_exp2(m_run - m_use);
+          l_run *= alpha;
+          if constexpr (Q8) l16_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = fast_exp2(__builtin_fmaf(s0[r], kmul, -m_use));
+          psum += s0[r];
+        }
       }
       l_run += psum;
       PV8 p0, p1;

@@ -75,6 +75,8 @@ struct mpaOperation {
   uint64_t plan_bytes = 0;
   std::vector<size_t> plan_offs;
   uint64_t ws_bytes = 0;       // workspace bytes an execution needs
+  uint64_t tile_f32_off = 0;   // prefill: fp32 tile copy at this workspace offset, if any
+  bool tile_f32 = false;
   mpa::LaunchEvents events{};  // timing hooks (mpaOperationSetLaunchEvents)
 
   ~mpaOperation() {
@@ -267,6 +269,13 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
     return st;
   }
   o->ws_bytes = o->plan_bytes;
+  // (right / left ALiBi tiles on the direct-load kernel: their fp32 copy follows the plan)
+  const size_t tile_f32 = mpa::prefill_tile_f32_bytes(headSize, shift_of(blockSize), o->mask_type, maskStride);
+  if (tile_f32 > 0) {
+    o->tile_f32 = true;
+    o->tile_f32_off = o->ws_bytes;
+    o->ws_bytes += align_up(tile_f32);
+  }
   mpa::PrefillParams& p = o->pp;
   p.q = query;
   p.k = key;
@@ -369,6 +378,7 @@ mpaStatus mpaSelfAttentionPrefixEncoder(void* workspace, uint64_t workspaceSize,
   mpa::PrefillParams p = op->pp;
   p.items = (const int4*)((char*)workspace + op->plan_offs[0]);
   p.seqs = (const int4*)((char*)workspace + op->plan_offs[1]);
+  p.mask_f32 = op->tile_f32 ? (float*)((char*)workspace + op->tile_f32_off) : nullptr;
   hipError_t e = mpa::launch_prefill(p, op->dtype, op->head_size, op->mask_type, op->grid,
                                      (hipStream_t)stream, op->events);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");

@@ -26,6 +26,8 @@ struct PrefillParams {
   int chunk;                   // chunk size of the chunked local mask (mask 10), else 0
   const void* mask;            // compressed mask tile (mask_type | kMaskTileFlag), else null
   int mask_stride;             // elements per tile row (128 or 256)
+  float* mask_f32;             // workspace copy of the tile in fp32 where
+                               // prefill_tile_f32_bytes() > 0, filled by each execution
   float scale2;                // qkScale * log2(e)
 };
 
@@ -33,6 +35,16 @@ struct PrefillParams {
 // | kMaskTileFlag; the tile grid is kMaskTile absolute positions.
 constexpr int kMaskTileFlag = 16;
 constexpr int kMaskTile = 128;
+
+// Workspace bytes of the fp32 copy of a right or left-aligned ALiBi tile that the
+// direct-load kernel (headSize 128, power-of-two blockSize >= 16) reads in place
+// of the caller's fp16/bf16 tile: one conversion per entry and execution instead
+// of one per score.  0 where the kernel reads the tile as given.
+inline size_t prefill_tile_f32_bytes(int head_size, int bs_shift, int mask_type, int mask_stride) {
+  const bool dma = head_size == 128 && bs_shift >= 4;
+  const bool linear_tile = mask_type == (kMaskTileFlag | 3) || mask_type == (kMaskTileFlag | 5);
+  return dma && linear_tile ? (size_t)mask_stride * (size_t)mask_stride * sizeof(float) : 0;
+}
 
 // Events a call records on its own kernels' dispatch packets (hipExtLaunchKernel):
 // start when its first kernel starts, stop when its last kernel ends; null = none.

@@ -449,6 +449,11 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   constexpr bool kAlibiLinear = !kTile && (kType == 3 || kType == 5);  // generated ALiBi bias
   constexpr bool kAlibiSqrt = !kTile && kType == 4;
   constexpr bool kTileAlibi = kTile && (kType == 3 || kType == 4 || kType == 5);
+  // right / left ALiBi tiles come as the execution's fp32 copy of the caller's
+  // tile (p.mask points at it); the norm and sqrt tiles in the input type
+  constexpr bool kTileF32 = kTile && (kType == 3 || kType == 5);
+  using MT = std::conditional_t<kTileF32, float, T>;
+  using MV4 = MT __attribute__((ext_vector_type(4)));
   constexpr bool kReverse = kType == 3 || kType == 4 || kType == 5;
   constexpr bool kChunked = kType == 10;  // causal inside chunks of p.chunk keys
   constexpr int NC = D / 16;              // 16-wide contraction chunks of QK^T
@@ -645,7 +650,7 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   // iteration; the ALiBi tiles for every tile, one iteration ahead, so that the
   // wait that ends an iteration has them in place and none is needed before
   // the softmax (it would drain the next tile's direct loads).
-  V4 mtv[8];
+  MV4 mtv[8];
   int mdk = 0;
   // ALiBi tiles: the block shift of this tile's entries (times slope2 for the
   // linear types)
@@ -656,8 +661,8 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   unsigned mrow_off = 0;
   unsigned mback_off = 0;
   if constexpr (kTile) {
-    mrow_off = ((unsigned)(a_lane - a_bq * kMaskTile) * (unsigned)p.mask_stride + 4u * g) * (unsigned)sizeof(T);
-    mback_off = kType == 9 ? 0u : (unsigned)kMaskTile * (unsigned)p.mask_stride * (unsigned)sizeof(T);
+    mrow_off = ((unsigned)(a_lane - a_bq * kMaskTile) * (unsigned)p.mask_stride + 4u * g) * (unsigned)sizeof(MT);
+    mback_off = kType == 9 ? 0u : (unsigned)kMaskTile * (unsigned)p.mask_stride * (unsigned)sizeof(MT);
   }
   auto needs_tile_mask = [&](int t) { return kTileAlibi || (kTile && t * kBN + kBN > w_full_keys); };
   auto load_tile_mask = [&](int t) __attribute__((always_inline)) {
@@ -671,10 +676,10 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
       mshift = mdk > 0 ? -(float)(kMaskTile * (mdk - 1)) : 0.0f;
       if constexpr (kType == 3) mshift *= slope2;
     }
-    const unsigned off = mrow_off + (mdk == 0 ? 0u : mback_off) + (unsigned)(j0 & (kMaskTile - 1)) * (unsigned)sizeof(T);
+    const unsigned off = mrow_off + (mdk == 0 ? 0u : mback_off) + (unsigned)(j0 & (kMaskTile - 1)) * (unsigned)sizeof(MT);
     const char* base = (const char*)p.mask;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mtv[u] = *(const V4*)(base + off + 16 * u);
+    for (int u = 0; u < 8; ++u) mtv[u] = *(const MV4*)(base + off + 8 * (int)sizeof(MT) * u);
   };
 
   // P of tile t from S^T (in s): running max and sum (see the comment above).
@@ -1008,20 +1013,49 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   }
 }
 
+// fp32 copy of a compressed tile: entry i of src to dst[i], 4 per lane (n4 groups).
+template <typename T>
+__global__ void __launch_bounds__(256) tile_to_f32_kernel(const T* __restrict__ src, float* __restrict__ dst,
+                                                          int n4) {
+  using V4 = typename Vec<T>::x4;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const V4 v = ((const V4*)src)[i];
+  float4 f;
+  f.x = (float)v[0];
+  f.y = (float)v[1];
+  f.z = (float)v[2];
+  f.w = (float)v[3];
+  ((float4*)dst)[i] = f;
+}
+
+// The direct-load kernel over a right or left-aligned ALiBi tile: the tile's
+// fp32 copy into p.mask_f32, then the attention reading it.  The call's start
+// event goes on the copy, its stop event on the attention.
+template <typename T, int MASK>
+hipError_t launch_f32_tile(const PrefillParams& p, dim3 g, hipStream_t s, const LaunchEvents& ev) {
+  if (p.mask_f32 == nullptr || p.mask == nullptr) return hipErrorInvalidValue;
+  const int n4 = p.mask_stride * p.mask_stride / 4;
+  hipExtLaunchKernelGGL(tile_to_f32_kernel<T>, dim3((n4 + 255) / 256), dim3(256), 0, s, ev.start, nullptr, 0,
+                        (const T*)p.mask, p.mask_f32, n4);
+  PrefillParams q = p;
+  q.mask = p.mask_f32;
+  hipExtLaunchKernelGGL((prefill_dma_kernel<T, MASK>), g, dim3(256), 0, s, nullptr, ev.stop, 0, q, p.block_tables);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStream_t s, const LaunchEvents& ev) {
   const dim3 g(grid), blk(256);
   if (D == 128 && p.bs_shift >= 4) {
     switch (mask_type) {
       case kMaskTileFlag | 3:
-        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 3>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
-        break;
+        return launch_f32_tile<T, kMaskTileFlag | 3>(p, g, s, ev);
       case kMaskTileFlag | 4:
         hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 4>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;
       case kMaskTileFlag | 5:
-        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 5>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
-        break;
+        return launch_f32_tile<T, kMaskTileFlag | 5>(p, g, s, ev);
       case kMaskTileFlag | 9:
         hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 9>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
         break;

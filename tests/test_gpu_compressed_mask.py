@@ -135,3 +135,28 @@ def test_alibi_tile_zero_and_negative_slopes(mask_type):
     c = dataclasses.replace(c, mask_tile=W.compressed_tile(mask_type, "bf16", 31)).to(DEV)
     out, lse = gpu_prefill(c)
     check_prefill_full(c, out, lse)
+
+
+@pytest.mark.parametrize("mask_type", [3, 4, 5])
+def test_tile_contents_read_at_each_execution(mask_type):
+    # one planned call run twice, the tile overwritten in place between the runs:
+    # each run follows the tile it found (right / left tiles on the direct-load
+    # kernel go through the execution's fp32 copy of the tile)
+    import masked_paged_attention_amd as mpa
+    log(f"case compressed tile rewritten between two executions mask={mask_type}")
+    c = W.make_prefill(260 + mask_type, np.array([300, 129]), np.array([700, 129]), 8, 2, 128, 128, "bf16",
+                       mask_type, 1.0 / np.sqrt(128), slopes="alibi", poison=True, name=f"rerun{mask_type}")
+    t1 = W.compressed_tile(mask_type, "bf16")
+    t2 = W.compressed_tile(mask_type, "bf16", 41)
+    c = c.to(DEV)
+    tile = t1.to(DEV).clone()
+    op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
+                           mask_type=c.mask_type, qk_scale=c.qk_scale,
+                           slopes=torch.as_tensor(c.slopes, device=DEV), return_lse=True,
+                           compressed_mask=tile)
+    for t in (t1, t2):
+        tile.copy_(t.to(DEV))
+        out, lse = op.run()
+        torch.cuda.synchronize()
+        check_prefill_full(dataclasses.replace(c, mask_tile=t), out.clone(), lse.clone())
+    op.close()

@@ -170,7 +170,7 @@ mpaStatus mpaSelfAttentionPrefixEncoderChunkedGetWorkspaceSize(
  * the generated mask of the same maskType.  A row whose tile hides every key
  * gets out = 0 and lse = -inf.  Phase 2 is mpaSelfAttentionPrefixEncoder; the operation keeps the
  * mask pointer, which must stay valid until the launches that use it end.
- * For maskType 3 and 5 with headSize 128 and a power-of-two blockSize >= 16,
+ * For maskType 3, 4 and 5 with headSize 128 and a power-of-two blockSize >= 16,
  * the workspace also holds an fp32 copy of the tile (256 KB after the plan),
  * which each execution fills from `mask` in a launch of its own before the
  * attention launch; the tile's contents are read at execution, not here.
@@ -185,7 +185,7 @@ mpaStatus mpaSelfAttentionPrefixEncoderCompressedMaskGetWorkspaceSize(
 
 /* PrefixEncoder, phase 2: copy of the plan into `workspace` (dev, >= the size
  * phase 1 returned, 256-byte aligned) and one kernel launch (two for the
- * compressed right / left ALiBi tiles that get an fp32 copy), all on `stream`
+ * compressed ALiBi tiles that get an fp32 copy), all on `stream`
  * (hipStream_t).  Errors: MPA_ERROR_INVALID_ARG for a NULL or misaligned
  * workspace or another kind of operation, MPA_ERROR_WORKSPACE_TOO_SMALL,
  * MPA_ERROR_HIP if the copy or the launch fails. */

@@ -269,7 +269,7 @@ mpaStatus make_prefill_op(const void* query, const void* key, const void* value,
     return st;
   }
   o->ws_bytes = o->plan_bytes;
-  // (right / left ALiBi tiles on the direct-load kernel: their fp32 copy follows the plan)
+  // (ALiBi tiles on the direct-load kernel: their fp32 copy follows the plan)
   const size_t tile_f32 = mpa::prefill_tile_f32_bytes(headSize, shift_of(blockSize), o->mask_type, maskStride);
   if (tile_f32 > 0) {
     o->tile_f32 = true;

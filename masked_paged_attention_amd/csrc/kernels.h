@@ -36,14 +36,14 @@ struct PrefillParams {
 constexpr int kMaskTileFlag = 16;
 constexpr int kMaskTile = 128;
 
-// Workspace bytes of the fp32 copy of a right or left-aligned ALiBi tile that the
+// Workspace bytes of the fp32 copy of an ALiBi tile (right, sqrt, left) that the
 // direct-load kernel (headSize 128, power-of-two blockSize >= 16) reads in place
 // of the caller's fp16/bf16 tile: one conversion per entry and execution instead
 // of one per score.  0 where the kernel reads the tile as given.
 inline size_t prefill_tile_f32_bytes(int head_size, int bs_shift, int mask_type, int mask_stride) {
   const bool dma = head_size == 128 && bs_shift >= 4;
-  const bool linear_tile = mask_type == (kMaskTileFlag | 3) || mask_type == (kMaskTileFlag | 5);
-  return dma && linear_tile ? (size_t)mask_stride * (size_t)mask_stride * sizeof(float) : 0;
+  const bool alibi_tile = mask_type == (kMaskTileFlag | 3) || mask_type == (kMaskTileFlag | 4) || mask_type == (kMaskTileFlag | 5);
+  return dma && alibi_tile ? (size_t)mask_stride * (size_t)mask_stride * sizeof(float) : 0;
 }
 
 // Events a call records on its own kernels' dispatch packets (hipExtLaunchKernel):

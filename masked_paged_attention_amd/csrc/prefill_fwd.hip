@@ -449,9 +449,9 @@ __global__ void __launch_bounds__(256, 2) prefill_dma_kernel(PrefillParams p,
   constexpr bool kAlibiLinear = !kTile && (kType == 3 || kType == 5);  // generated ALiBi bias
   constexpr bool kAlibiSqrt = !kTile && kType == 4;
   constexpr bool kTileAlibi = kTile && (kType == 3 || kType == 4 || kType == 5);
-  // right / left ALiBi tiles come as the execution's fp32 copy of the caller's
-  // tile (p.mask points at it); the norm and sqrt tiles in the input type
-  constexpr bool kTileF32 = kTile && (kType == 3 || kType == 5);
+  // ALiBi tiles come as the execution's fp32 copy of the caller's tile (p.mask
+  // points at it); the norm tile in the input type
+  constexpr bool kTileF32 = kTile && (kType == 3 || kType == 4 || kType == 5);
   using MT = std::conditional_t<kTileF32, float, T>;
   using MV4 = MT __attribute__((ext_vector_type(4)));
   constexpr bool kReverse = kType == 3 || kType == 4 || kType == 5;
@@ -1029,7 +1029,7 @@ __global__ void __launch_bounds__(256) tile_to_f32_kernel(const T* __restrict__ 
   ((float4*)dst)[i] = f;
 }
 
-// The direct-load kernel over a right or left-aligned ALiBi tile: the tile's
+// The direct-load kernel over an ALiBi tile (right, sqrt, left): the tile's
 // fp32 copy into p.mask_f32, then the attention reading it.  The call's start
 // event goes on the copy, its stop event on the attention.
 template <typename T, int MASK>
@@ -1052,8 +1052,7 @@ hipError_t launch_mask(const PrefillParams& p, int mask_type, int grid, hipStrea
       case kMaskTileFlag | 3:
         return launch_f32_tile<T, kMaskTileFlag | 3>(p, g, s, ev);
       case kMaskTileFlag | 4:
-        hipExtLaunchKernelGGL((prefill_dma_kernel<T, kMaskTileFlag | 4>), g, blk, 0, s, ev.start, ev.stop, 0, p, p.block_tables);
-        break;
+        return launch_f32_tile<T, kMaskTileFlag | 4>(p, g, s, ev);
       case kMaskTileFlag | 5:
         return launch_f32_tile<T, kMaskTileFlag | 5>(p, g, s, ev);
       case kMaskTileFlag | 9:

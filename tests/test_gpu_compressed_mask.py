@@ -140,7 +140,7 @@ def test_alibi_tile_zero_and_negative_slopes(mask_type):
 @pytest.mark.parametrize("mask_type", [3, 4, 5])
 def test_tile_contents_read_at_each_execution(mask_type):
     # one planned call run twice, the tile overwritten in place between the runs:
-    # each run follows the tile it found (right / left tiles on the direct-load
+    # each run follows the tile it found (ALiBi tiles on the direct-load
     # kernel go through the execution's fp32 copy of the tile)
     import masked_paged_attention_amd as mpa
     log(f"case compressed tile rewritten between two executions mask={mask_type}")

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads.gen as W
-from tests.gpu_helpers import check_prefill_full, gpu_prefill, log
+from tests.gpu_helpers import check_prefill_full, check_prefill_heads, gpu_prefill, log
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -160,3 +160,22 @@ def test_tile_contents_read_at_each_execution(mask_type):
         torch.cuda.synchronize()
         check_prefill_full(dataclasses.replace(c, mask_tile=t), out.clone(), lse.clone())
     op.close()
+
+
+@pytest.mark.parametrize("bias_seed", [None, 43])
+def test_sqrt_tile_long_sequence(bias_seed):
+    # the sqrt tile over 8192 positions, every row of three heads: key blocks up
+    # to 63 behind a row's own 128-block, with the page's tile (distances 1..255
+    # behind the diagonal) and with an extra bias on it that widens them (no
+    # -inf behind the diagonal)
+    log(f"case sqrt tile, 8192 tokens, extra bias seed {bias_seed}")
+    c = W.make_prefill(270, np.array([8192]), np.array([8192]), 4, 4, 128, 128, "bf16", 4,
+                       1.0 / np.sqrt(128), slopes="alibi", poison=True, name=f"sqrtfar{bias_seed}")
+    tile = W.compressed_tile(4, "bf16")
+    if bias_seed is not None:
+        rng = np.random.default_rng(bias_seed)
+        extra = torch.as_tensor(-0.25 * rng.integers(0, 200, size=tuple(tile.shape)), dtype=torch.float32)
+        tile = (tile.float() + extra).to(tile.dtype)
+    c = dataclasses.replace(c, mask_tile=tile).to(DEV)
+    out, lse = gpu_prefill(c)
+    check_prefill_heads(c, out, lse, [0, 1, 3])

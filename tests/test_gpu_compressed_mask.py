@@ -179,3 +179,24 @@ def test_sqrt_tile_long_sequence(bias_seed):
     c = dataclasses.replace(c, mask_tile=tile).to(DEV)
     out, lse = gpu_prefill(c)
     check_prefill_heads(c, out, lse, [0, 1, 3])
+
+
+@pytest.mark.parametrize("mask_type,D,bs", [(3, 128, 128), (4, 128, 16), (5, 128, 64), (9, 128, 128),
+                                            (3, 64, 64), (4, 128, 24)])
+def test_compressed_mask_workspace_size(mask_type, D, bs):
+    # the workspace holds the launch plan, and for the ALiBi tiles on the
+    # direct-load kernel (headSize 128, power-of-two blockSize >= 16) the tile's
+    # 256 KB fp32 copy after it; other shapes read the tile in place
+    import masked_paged_attention_amd as mpa
+    log(f"case compressed-mask workspace size mask={mask_type} D={D} bs={bs}")
+    L, kv = np.array([300, 129]), np.array([700, 129])
+    c = W.make_prefill(280 + mask_type, L, kv, 4, 2, D, bs, "bf16", mask_type, 1.0 / np.sqrt(D),
+                       slopes="alibi" if mask_type != 9 else None, poison=False, name="ws").to(DEV)
+    tile = W.compressed_tile(mask_type, "bf16").to(DEV)
+    slopes = None if c.slopes is None else torch.as_tensor(c.slopes, device=DEV)
+    op = mpa.PrefixEncoder(c.query, c.key, c.value, c.block_tables, c.seq_len, c.kv_seq_len,
+                           mask_type=mask_type, qk_scale=c.qk_scale, slopes=slopes, compressed_mask=tile)
+    plan_ws = mpa.plan_prefill(L, kv, mask_type, 4, 2, head_size=D, with_workspace=True)[-1]
+    copy = 256 * 256 * 4 if (mask_type != 9 and D == 128 and bs >= 16 and bs & (bs - 1) == 0) else 0
+    assert op.workspace.numel() == plan_ws + copy
+    op.close()
